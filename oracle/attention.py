@@ -1,0 +1,119 @@
+"""Oracle for masked softmax attention (TEST INFRASTRUCTURE ONLY; see package doc).
+
+Plain float64 numpy.  Inputs are the exact values of the bf16 tensors the
+GPU path receives (converted losslessly to float64); nothing is rounded on
+the way.
+
+Definitions followed (review Prompt 1.3.1, Step 0; paper §3 Eq.1 and Eq.2,
+whose bodies were lost in extraction but are the standard forms):
+
+* logits z[q, k] = scale * <Q[q], K[k]> for the keys k the mask allows, and
+  -inf for the others (the mask M is added to the logits);
+* P = softmax over k of z, O = P V, and LSE[q] = log sum_k exp(z[q, k])
+  (natural log), i.e. LSE = m + log(sum exp(z - m)) with m = max_k z;
+* gradients of O with respect to Q, K, V for an upstream gradient dO are the
+  textbook ones: dV = P^T dO, dP = dO V^T, Delta[q] = sum_k P[q,k] dP[q,k]
+  (= <dO[q], O[q]>), dS = P * (dP - Delta), dQ = scale dS K,
+  dK = scale dS^T Q.
+
+The mask is given as a set of key columns per query tile ("tile semantics",
+review Step 5, paper §4.2: every token of a kept block is computed), or as a
+boolean token mask for small problems.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+
+def tile_columns(kept_row: np.ndarray, n: int, T: int) -> np.ndarray:
+    """Key token indices of the kept tiles in one row of the tile map."""
+    tiles = np.nonzero(kept_row)[0]
+    cols = (tiles[:, None] * T + np.arange(T)[None, :]).reshape(-1)
+    return cols[cols < n]
+
+
+def _softmax_rows(z: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    m = z.max(axis=1, keepdims=True)
+    e = np.exp(z - m)
+    l = e.sum(axis=1, keepdims=True)
+    p = e / l
+    lse = (m + np.log(l))[:, 0]
+    # every softmax row sums to one (review Step 0: P is a distribution)
+    assert np.all(np.abs(p.sum(axis=1) - 1.0) < 1e-9)
+    return p, lse
+
+
+def fwd_tile(q: np.ndarray, k: np.ndarray, v: np.ndarray, kept: np.ndarray,
+             T: int, scale: float, u: int) -> tuple[np.ndarray, np.ndarray]:
+    """O and LSE for the query rows of tile u of one (batch, head).
+
+    q, k, v: float64 [n, D].  kept: boolean [nb, nb] tile map.
+    Returns O [rows, D] and LSE [rows] with rows = the valid rows of tile u.
+    """
+    n = q.shape[0]
+    rows = slice(u * T, min(n, (u + 1) * T))
+    cols = tile_columns(kept[u], n, T)
+    z = scale * (q[rows] @ k[cols].T)
+    p, lse = _softmax_rows(z)
+    return p @ v[cols], lse
+
+
+def fwd(q: np.ndarray, k: np.ndarray, v: np.ndarray, kept: np.ndarray,
+        T: int, scale: float, tiles=None) -> tuple[np.ndarray, np.ndarray]:
+    """O [n, D] and LSE [n] for one (batch, head) under the tile map.
+
+    ``tiles``: optional list of query tiles to compute; rows of other tiles
+    are left as NaN.
+    """
+    n, d = q.shape
+    nb = kept.shape[0]
+    o = np.full((n, d), np.nan)
+    lse = np.full(n, np.nan)
+    for u in (range(nb) if tiles is None else tiles):
+        rows = slice(u * T, min(n, (u + 1) * T))
+        o[rows], lse[rows] = fwd_tile(q, k, v, kept, T, scale, u)
+    return o, lse
+
+
+def fwd_masked(q: np.ndarray, k: np.ndarray, v: np.ndarray, mask: np.ndarray,
+               scale: float) -> tuple[np.ndarray, np.ndarray]:
+    """O and LSE for one (batch, head) under a boolean token mask [n, n]
+    (True = allowed).  Every row must allow at least one key."""
+    z = scale * (q @ k.T)
+    z = np.where(mask, z, -np.inf)
+    p, lse = _softmax_rows(z)
+    return p @ v, lse
+
+
+def bwd(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray,
+        kept: np.ndarray, T: int, scale: float):
+    """dQ, dK, dV [n, D] for one (batch, head) under the tile map."""
+    n, d = q.shape
+    nb = kept.shape[0]
+    dq = np.zeros((n, d))
+    dk = np.zeros((n, d))
+    dv = np.zeros((n, d))
+    for u in range(nb):
+        rows = slice(u * T, min(n, (u + 1) * T))
+        cols = tile_columns(kept[u], n, T)
+        z = scale * (q[rows] @ k[cols].T)
+        p, _ = _softmax_rows(z)
+        dp = do[rows] @ v[cols].T
+        delta = (p * dp).sum(axis=1, keepdims=True)
+        ds = p * (dp - delta)
+        dv[cols] += p.T @ do[rows]
+        dq[rows] += scale * (ds @ k[cols])
+        dk[cols] += scale * (ds.T @ q[rows])
+    return dq, dk, dv
+
+
+def bwd_masked(q, k, v, do, mask, scale):
+    """dQ, dK, dV for one (batch, head) under a boolean token mask [n, n]."""
+    z = scale * (q @ k.T)
+    z = np.where(mask, z, -np.inf)
+    p, _ = _softmax_rows(z)
+    dp = do @ v.T
+    delta = (p * dp).sum(axis=1, keepdims=True)
+    ds = p * (dp - delta)
+    return scale * (ds @ k), scale * (ds.T @ q), p.T @ do

@@ -1,0 +1,237 @@
+"""Oracle for the radial static mask (TEST INFRASTRUCTURE ONLY; see package doc).
+
+Token indexing follows the review, Prompt 1.3.1 "Terms and variables": a video
+of f frames with s tokens per frame has n = f*s tokens; token q = i*s + a is
+position a (row-major inside the frame) of frame i.  The 4-D mask
+M~[i, j, a, b] is flattened to the 2-D mask M[i*s + a, j*s + b] (review,
+Step 3; paper Eq.4, §4.2).
+
+Readings taken where the extracted text lost the formulas (each is listed
+with its reason in the design notes):
+
+* band index   r = floor(log2(max(|i-j|, 1)))            (review toy example,
+  parts A-C; paper §4.2 Fig.5a).  Computed with the integer bit length, never
+  with a float log2.
+* half width   w = floor(s / 2**r)                        (review toy example;
+  paper §4.2 Fig.5b "half-diagonal width").
+* spatial test |a - b| < w on the row-major in-frame index (review toy
+  example part C: k0=4, w=4 admits l=1..7, so the edge is strict).
+* width below one (w == 0): keep only the diagonal a == b, and only for frame
+  pairs whose distance is a multiple of ceil(2**r / s), so the amortised
+  density of that band is about 1/2**r, the same decay as the bands above it
+  (review Step 2-C; paper Fig.5 caption, Eq.4; rebuttal "Whether to Reduce
+  the Diagonal Frequency when the Width is below 1").
+* attention sink: every query may attend every key of frame 0 (review Step 4;
+  paper §4.2, Appx A.1 Eq.8).  Column sink only.
+* tile semantics: a T x T tile of the n x n mask is kept when at least one
+  allowed token pair falls in it, and a kept tile is computed in full (review
+  Step 5; paper §4.2: block-wise computation with 128x128 blocks).
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+
+# ----------------------------------------------------------------------------
+# Band table (review toy example A-C; paper §4.2 Fig.5a/5b; Fig.5 caption)
+# ----------------------------------------------------------------------------
+
+def band_index(delta: int) -> int:
+    """r = floor(log2(max(delta, 1))) for an integer frame distance delta >= 0."""
+    if delta < 0:
+        raise ValueError("frame distance must be >= 0")
+    return max(int(delta), 1).bit_length() - 1
+
+
+def band(delta: int, s: int) -> tuple[int, int, int]:
+    """(r, w, q) for frame distance delta and s tokens per frame.
+
+    r: band index; w = floor(s / 2**r): half width of the kept diagonal;
+    q: diagonal sampling period, only meaningful when w == 0, where a frame
+    pair at distance delta keeps its diagonal iff delta % q == 0, with
+    q = ceil(2**r / s).  For w >= 1 the period is 1 (no sampling).
+    """
+    r = band_index(delta)
+    w = s // (2 ** r)
+    if w >= 1:
+        q = 1
+    else:
+        q = -(-(2 ** r) // s)  # ceil(2**r / s) in integers
+    return r, w, q
+
+
+def band_table(f: int, s: int) -> np.ndarray:
+    """int64 array [f, 3] with (r, w, q) for every frame distance 0..f-1."""
+    return np.array([band(d, s) for d in range(f)], dtype=np.int64).reshape(f, 3)
+
+
+# ----------------------------------------------------------------------------
+# Token predicate and brute-force mask (review Step 2-4; paper Eq.4, Eq.8)
+# ----------------------------------------------------------------------------
+
+def allowed(q: int, k: int, s: int, sink: bool = True) -> bool:
+    """True iff query token q may attend key token k (scalar, plain Python)."""
+    i, a = divmod(q, s)
+    j, b = divmod(k, s)
+    if sink and j == 0:
+        return True
+    delta = abs(i - j)
+    r, w, period = band(delta, s)
+    if w >= 1:
+        return abs(a - b) < w
+    return a == b and delta % period == 0
+
+
+def token_mask(f: int, s: int, sink: bool = True) -> np.ndarray:
+    """Brute-force boolean mask [n, n] (n = f*s), True = allowed.
+
+    Evaluates the same predicate as ``allowed`` for every pair at once; meant
+    for n up to a few thousand.
+    """
+    n = f * s
+    if n > 16384:
+        raise ValueError("token_mask is brute force; n must be <= 16384")
+    idx = np.arange(n)
+    i, a = np.divmod(idx, s)
+    delta = np.abs(i[:, None] - i[None, :])
+    tab = band_table(f, s)
+    w = tab[delta, 1]
+    period = tab[delta, 2]
+    sep = np.abs(a[:, None] - a[None, :])
+    near = sep < w
+    diag = (sep == 0) & (delta % period == 0)
+    m = np.where(w >= 1, near, diag)
+    if sink:
+        m = m | (i[None, :] == 0)
+    return m
+
+
+def closed_form_pairs(f: int, s: int, sink: bool = True) -> int:
+    """Number of allowed token pairs, counted per frame pair in closed form.
+
+    For a frame pair at distance delta with half width w >= 1, the number of
+    (a, b) in [0, s)^2 with |a - b| < w is s*(2w-1) - w*(w-1) (a band of
+    2w-1 diagonals minus the two clipped corner triangles; w <= s always).
+    With w == 0 it is s when delta is a multiple of the sampling period, else
+    0.  There are f frame pairs at distance 0 and 2*(f - delta) at distance
+    delta > 0.  The sink adds, for every query frame i != 0, the pairs of
+    frame 0 that the band did not already allow.
+    """
+    def per_pair(delta: int) -> int:
+        r, w, period = band(delta, s)
+        if w >= 1:
+            return s * (2 * w - 1) - w * (w - 1)
+        return s if delta % period == 0 else 0
+
+    total = f * per_pair(0)
+    for d in range(1, f):
+        total += 2 * (f - d) * per_pair(d)
+    if sink:
+        # each query frame i >= 1 gains the full frame 0 (s*s pairs) minus
+        # what band(i) already allowed toward frame 0
+        for i in range(1, f):
+            total += s * s - per_pair(i)
+    return total
+
+
+# ----------------------------------------------------------------------------
+# Tile cover (review Step 5; paper §4.2 "128x128 blocks")
+# ----------------------------------------------------------------------------
+
+def n_blocks(n: int, T: int) -> int:
+    return -(-n // T)
+
+
+def kept_tiles(f: int, s: int, T: int, sink: bool = True) -> np.ndarray:
+    """Boolean [nb, nb] tile map: kept[u, v] iff some allowed (q, k) has
+    q // T == u and k // T == v.
+
+    Built by sweeping every (query token, key frame) pair: the keys of frame j
+    that query q = (i, a) may attend form one contiguous run of positions
+    (|a - b| < w, or the single b == a, or all of frame 0 for the sink), so
+    they cover a contiguous run of key tiles.  Each run is marked in a
+    per-query-tile difference array and a prefix sum gives the union.
+    """
+    n = f * s
+    nb = n_blocks(n, T)
+    tab = band_table(f, s)
+    qtok = np.arange(n, dtype=np.int64)
+    qi, qa = np.divmod(qtok, s)
+    qtile = qtok // T
+    cover = np.zeros((nb, nb + 1), dtype=np.int64)
+    flat = cover.reshape(-1)
+    starts: list[np.ndarray] = []
+    ends: list[np.ndarray] = []
+    pending = 0
+    for j in range(f):
+        delta = np.abs(qi - j)
+        w = tab[delta, 1]
+        period = tab[delta, 2]
+        lo = np.where(w >= 1, np.maximum(qa - w + 1, 0), qa)
+        hi = np.where(w >= 1, np.minimum(qa + w - 1, s - 1), qa)
+        has = (w >= 1) | (delta % period == 0)
+        if sink and j == 0:
+            lo = np.zeros_like(qa)
+            hi = np.full_like(qa, s - 1)
+            has = np.ones_like(has)
+        klo = (j * s + lo) // T
+        khi = (j * s + hi) // T
+        rows = qtile[has]
+        starts.append(rows * (nb + 1) + klo[has])
+        ends.append(rows * (nb + 1) + khi[has] + 1)
+        pending += rows.size
+        if pending > 8_000_000 or j == f - 1:
+            flat += np.bincount(np.concatenate(starts), minlength=flat.size)
+            flat -= np.bincount(np.concatenate(ends), minlength=flat.size)
+            starts, ends, pending = [], [], 0
+    return np.cumsum(cover, axis=1)[:, :nb] > 0
+
+
+def kept_tiles_bruteforce(mask: np.ndarray, T: int) -> np.ndarray:
+    """OR-reduce a token mask [n, n] over T x T tiles (ragged last tile)."""
+    n = mask.shape[0]
+    nb = n_blocks(n, T)
+    pad = nb * T - n
+    m = np.pad(mask, ((0, pad), (0, pad)))
+    return m.reshape(nb, T, nb, T).any(axis=(1, 3))
+
+
+def csr(kept: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """CSR of the kept map: per query tile, ascending kept key tiles."""
+    counts = kept.sum(axis=1)
+    row_ptr = np.zeros(kept.shape[0] + 1, dtype=np.int64)
+    row_ptr[1:] = np.cumsum(counts)
+    col_idx = np.nonzero(kept)[1]
+    return row_ptr, col_idx.astype(np.int64)
+
+
+def csc(kept: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """CSC of the kept map: per key tile, ascending query tiles."""
+    return csr(kept.T)
+
+
+def tile_pairs(kept: np.ndarray, n: int, T: int) -> int:
+    """Valid token pairs inside kept tiles (rows and columns clipped to n)."""
+    nb = kept.shape[0]
+    size = np.full(nb, T, dtype=np.int64)
+    size[-1] = n - (nb - 1) * T
+    return int(size @ kept.astype(np.int64) @ size)
+
+
+def effective_mask(f: int, s: int, T: int, sink: bool = True,
+                   mode: str = "tile") -> np.ndarray:
+    """Boolean [n, n] mask the attention uses (small n only).
+
+    mode "tile": every token pair inside a kept tile (tile semantics).
+    mode "token": exactly the allowed token pairs.
+    """
+    tok = token_mask(f, s, sink)
+    if mode == "token":
+        return tok
+    if mode != "tile":
+        raise ValueError(mode)
+    n = f * s
+    kept = kept_tiles_bruteforce(tok, T)
+    t = np.arange(n) // T
+    return kept[t[:, None], t[None, :]]

@@ -1,0 +1,143 @@
+"""Pins for the oracle's attention forward/backward (CPU only).
+
+The oracle is checked against library routines it does not use (torch's
+float64 scaled_dot_product_attention and autograd), against pure-Python
+loops on tiny inputs, finite differences and the V == 1 invariant.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention as oa
+from oracle import mask as om
+
+
+def _rand(shape, seed):
+    g = np.random.default_rng(seed)
+    return g.standard_normal(shape)
+
+
+def _sdpa(q, k, v, mask, scale):
+    tq, tk, tv = (torch.from_numpy(x)[None, None] for x in (q, k, v))
+    tm = torch.from_numpy(mask)[None, None]
+    o = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=tm, scale=scale)
+    return o[0, 0].numpy()
+
+
+def test_dense_limit_equals_sdpa():
+    # f = 2 covers every pair: radial attention reduces to plain attention
+    f, s, T, d = 2, 40, 16, 8
+    n = f * s
+    q, k, v = _rand((n, d), 1), _rand((n, d), 2), _rand((n, d), 3)
+    kept = om.kept_tiles(f, s, T, True)
+    assert kept.all()
+    o, lse = oa.fwd(q, k, v, kept, T, 0.3)
+    tq, tk, tv = (torch.from_numpy(x)[None, None] for x in (q, k, v))
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, scale=0.3)[0, 0].numpy()
+    np.testing.assert_allclose(o, ref, rtol=0, atol=1e-12)
+    ref_lse = torch.logsumexp(0.3 * torch.from_numpy(q) @ torch.from_numpy(k).T, dim=1).numpy()
+    np.testing.assert_allclose(lse, ref_lse, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("f,s,T", [(5, 7, 4), (8, 16, 16), (6, 9, 8)])
+def test_tile_mask_forward_equals_sdpa(f, s, T):
+    d = 6
+    n = f * s
+    q, k, v = _rand((n, d), 4), _rand((n, d), 5), _rand((n, d), 6)
+    kept = om.kept_tiles(f, s, T, True)
+    eff = om.effective_mask(f, s, T, True)
+    o, lse = oa.fwd(q, k, v, kept, T, 0.5)
+    np.testing.assert_allclose(o, _sdpa(q, k, v, eff, 0.5), rtol=0, atol=1e-12)
+    z = torch.from_numpy(0.5 * (q @ k.T)).masked_fill(~torch.from_numpy(eff), -math.inf)
+    np.testing.assert_allclose(lse, torch.logsumexp(z, 1).numpy(), rtol=0, atol=1e-12)
+
+
+def test_token_mask_forward_equals_sdpa():
+    f, s, d = 7, 6, 5
+    n = f * s
+    q, k, v = _rand((n, d), 7), _rand((n, d), 8), _rand((n, d), 9)
+    m = om.token_mask(f, s, True)
+    o, _ = oa.fwd_masked(q, k, v, m, 0.7)
+    np.testing.assert_allclose(o, _sdpa(q, k, v, m, 0.7), rtol=0, atol=1e-12)
+
+
+def test_forward_brute_force_loops():
+    # pure-Python double loop on a tiny case, one query at a time
+    f, s, T, d = 3, 4, 3, 3
+    n = f * s
+    q, k, v = _rand((n, d), 10), _rand((n, d), 11), _rand((n, d), 12)
+    kept = om.kept_tiles(f, s, T, False)
+    o, lse = oa.fwd(q, k, v, kept, T, 0.9)
+    for qi in range(n):
+        keys = [kj for kj in range(n) if kept[qi // T, kj // T]]
+        logits = [0.9 * sum(q[qi, x] * k[kj, x] for x in range(d)) for kj in keys]
+        mx = max(logits)
+        w = [math.exp(z - mx) for z in logits]
+        tot = sum(w)
+        for x in range(d):
+            assert abs(o[qi, x] - sum(wi * v[kj, x] for wi, kj in zip(w, keys)) / tot) < 1e-12
+        assert abs(lse[qi] - (mx + math.log(tot))) < 1e-12
+
+
+def test_v_ones_gives_ones():
+    f, s, T, d = 9, 8, 8, 4
+    n = f * s
+    q, k = _rand((n, d), 13), _rand((n, d), 14)
+    kept = om.kept_tiles(f, s, T, True)
+    o, _ = oa.fwd(q, k, np.ones((n, d)), kept, T, 1.0)
+    np.testing.assert_allclose(o, 1.0, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("f,s,T", [(5, 7, 4), (9, 4, 8), (2, 10, 8)])
+def test_backward_equals_autograd(f, s, T):
+    d = 5
+    n = f * s
+    q, k, v, do = (_rand((n, d), 20 + i) for i in range(4))
+    kept = om.kept_tiles(f, s, T, True)
+    eff = om.effective_mask(f, s, T, True)
+    scale = 0.6
+    dq, dk, dv = oa.bwd(q, k, v, do, kept, T, scale)
+    tq, tk, tv = (torch.from_numpy(x).requires_grad_(True) for x in (q, k, v))
+    z = (scale * tq @ tk.T).masked_fill(~torch.from_numpy(eff), -math.inf)
+    o = torch.softmax(z, dim=1) @ tv
+    o.backward(torch.from_numpy(do))
+    np.testing.assert_allclose(dq, tq.grad.numpy(), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dk, tk.grad.numpy(), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dv, tv.grad.numpy(), rtol=0, atol=1e-12)
+    # the token-mask variant agrees with autograd under the token mask
+    m = om.token_mask(f, s, True)
+    tq2, tk2, tv2 = (torch.from_numpy(x).requires_grad_(True) for x in (q, k, v))
+    z2 = (scale * tq2 @ tk2.T).masked_fill(~torch.from_numpy(m), -math.inf)
+    (torch.softmax(z2, dim=1) @ tv2).backward(torch.from_numpy(do))
+    g = oa.bwd_masked(q, k, v, do, m, scale)
+    for a, b in zip(g, (tq2.grad, tk2.grad, tv2.grad)):
+        np.testing.assert_allclose(a, b.numpy(), rtol=0, atol=1e-12)
+
+
+def test_backward_finite_differences():
+    # two frames (dense) and one with a sparse band: central differences of
+    # sum(O * dO) with respect to every input element
+    for f, s, T in [(2, 3, 2), (5, 2, 1)]:
+        d = 3
+        n = f * s
+        q, k, v, do = (_rand((n, d), 40 + i) for i in range(4))
+        kept = om.kept_tiles(f, s, T, False)
+        scale = 0.8
+        dq, dk, dv = oa.bwd(q, k, v, do, kept, T, scale)
+
+        def loss(q_, k_, v_):
+            o, _ = oa.fwd(q_, k_, v_, kept, T, scale)
+            return float((o * do).sum())
+
+        h = 1e-6
+        for arr, grad, which in ((q, dq, 0), (k, dk, 1), (v, dv, 2)):
+            for idx in np.ndindex(arr.shape):
+                args = [q.copy(), k.copy(), v.copy()]
+                args[which][idx] += h
+                up = loss(*args)
+                args[which][idx] -= 2 * h
+                dn = loss(*args)
+                assert abs((up - dn) / (2 * h) - grad[idx]) < 1e-7

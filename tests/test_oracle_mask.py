@@ -1,0 +1,195 @@
+"""Pins for the oracle's mask builder (CPU only).
+
+Each test checks ``oracle.mask`` against something other than itself: the
+review's worked toy example (golden fixture), a closed-form count checked
+against brute force, the O(n log n) claim, the power-of-two special case,
+symmetry and the halving of amortised density per band.
+"""
+
+import math
+import os
+
+import numpy as np
+import pytest
+
+from oracle import mask as om
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _read_toy():
+    bands, frame0, counts = [], None, {}
+    with open(os.path.join(GOLDEN, "toy_f4_s9.txt")) as fh:
+        for line in fh:
+            line = line.split("#")[0].split()
+            if not line:
+                continue
+            if line[0] == "band":
+                bands.append(tuple(int(x) for x in line[1:]))
+            elif line[0] == "frame0_keys":
+                frame0 = [int(x) for x in line[1:]]
+            else:
+                counts[line[0]] = int(line[1])
+    return bands, frame0, counts
+
+
+def test_toy_example_bands():
+    bands, _, _ = _read_toy()
+    assert len(bands) == 3
+    for delta, r, w in bands:
+        assert om.band(delta, 9)[:2] == (r, w)
+
+
+def test_toy_example_frame0_and_row_counts():
+    _, frame0, counts = _read_toy()
+    f, s = 4, 9
+    q = 2 * s + 4
+    got = [b for b in range(s) if om.allowed(q, 0 * s + b, s, sink=False)]
+    assert got == frame0
+    row_nosink = sum(om.allowed(q, k, s, sink=False) for k in range(f * s))
+    row_sink = sum(om.allowed(q, k, s, sink=True) for k in range(f * s))
+    assert row_nosink == counts["row_count_nosink"]
+    assert row_sink == counts["row_count_sink"]
+    # the vectorised brute-force mask agrees with the scalar predicate
+    m = om.token_mask(f, s, sink=False)
+    assert int(m[q].sum()) == counts["row_count_nosink"]
+
+
+def test_band_index_exact_at_powers_of_two():
+    # floor(log2) must not misround at 2**k or 2**k - 1
+    for k in range(0, 40):
+        assert om.band_index(2 ** k) == k
+        if k >= 1:
+            assert om.band_index(2 ** k - 1) == k - 1
+    assert om.band_index(0) == 0  # max(delta, 1) for the same frame
+
+
+def test_central_band_is_distance_one():
+    # rebuttal "Width of Central Band": the default central band covers
+    # |i - j| <= 1, i.e. r == 0 exactly for delta in {0, 1}
+    assert [om.band_index(d) for d in range(5)] == [0, 0, 1, 1, 2]
+
+
+def test_width_halves_per_band():
+    # rebuttal "Width Scale Between Consecutive Bands": scale 2
+    s = 3600
+    ws = [om.band(2 ** r, s)[1] for r in range(8)]
+    assert ws == [3600, 1800, 900, 450, 225, 112, 56, 28]
+
+
+@pytest.mark.parametrize("sink", [False, True])
+def test_closed_form_matches_brute_force(sink):
+    for f in list(range(1, 13)) + [17, 33, 37]:
+        for s in [1, 2, 3, 5, 9, 16]:
+            if f * s > 4000:
+                continue
+            m = om.token_mask(f, s, sink)
+            assert int(m.sum()) == om.closed_form_pairs(f, s, sink), (f, s, sink)
+
+
+def test_toy_total_pairs():
+    # 4 frames x 9 tokens: derived totals of the reading (1116 / 1176 of 1296)
+    assert om.closed_form_pairs(4, 9, False) == 1116
+    assert om.closed_form_pairs(4, 9, True) == 1176
+    assert int(om.token_mask(4, 9, True).sum()) == 1176
+
+
+def test_n_log_n_growth():
+    # abstract / review Fig.2: O(n log n) for fixed s and growing f.  The pair
+    # count divided by n*s*log2(2f) stays bounded while the dense count n*n
+    # divided by the same grows like f / log f.
+    s = 16
+    ratios = []
+    for f in [8, 16, 32, 64, 128, 256, 512]:
+        n = f * s
+        pairs = om.closed_form_pairs(f, s, sink=False)
+        ratios.append(pairs / (n * s * math.log2(2 * f)))
+        assert pairs <= 4 * n * s * (1 + math.log2(max(f, 2)))
+    assert max(ratios) < 3.0
+    dense_ratio = (512 * s) ** 2 / (512 * s * s * math.log2(1024))
+    assert dense_ratio > 10 * max(ratios)
+
+
+def test_density_constant_across_resolution():
+    # rebuttal "Complexity with Respect to Spatial Resolution": at a fixed
+    # number of frames the mask sparsity does not depend on resolution
+    f = 33
+    dens = [om.closed_form_pairs(f, s, True) / (f * s) ** 2 for s in [400, 900, 1600, 3600, 8100]]
+    assert max(dens) - min(dens) < 0.01
+
+
+def test_single_token_frames_give_power_of_two_distances():
+    # s == 1: every band has w < 1 beyond distance 1, the sampling keeps
+    # distance delta iff delta is a power of two (the LLM-style pattern the
+    # review's related-work list mentions)
+    f = 40
+    m = om.token_mask(f, 1, sink=False)
+    dists = sorted({abs(i - j) for i in range(f) for j in range(f) if m[i, j]})
+    assert dists == [0, 1, 2, 4, 8, 16, 32]
+
+
+def test_amortised_density_halves_below_unit_width():
+    # review Step 2-C: below unit width the diagonal is kept in a subsample
+    # of frame pairs so that the amortised density keeps halving per band.
+    # For s a power of two, over a whole band r (2**r >= s) the kept share of
+    # frame pairs times the diagonal density 1/s is exactly 2**-r.
+    for s in [1, 2, 4, 8]:
+        for r in range(int(math.log2(s)), 12):
+            kept = [d for d in range(2 ** r, 2 ** (r + 1))
+                    if om.band(d, s)[1] >= 1 or d % om.band(d, s)[2] == 0]
+            frac = len(kept) / 2 ** r
+            if om.band(2 ** r, s)[1] >= 1:
+                continue  # w >= 1: not the sampled regime
+            assert frac / s == pytest.approx(2.0 ** -r)
+
+
+def test_mask_symmetric_without_sink():
+    for f, s in [(5, 7), (9, 4), (17, 3)]:
+        m = om.token_mask(f, s, sink=False)
+        assert np.array_equal(m, m.T)
+
+
+def test_sink_column_block():
+    f, s = 6, 10
+    m = om.token_mask(f, s, sink=True)
+    assert m[:, :s].all()
+
+
+@pytest.mark.parametrize("sink", [False, True])
+def test_tile_sweep_matches_bruteforce(sink):
+    for f, s, T in [(4, 9, 4), (8, 16, 8), (8, 16, 64), (5, 7, 3), (33, 3, 16),
+                    (12, 1, 4), (6, 100, 64), (3, 50, 128), (40, 2, 7), (20, 33, 32)]:
+        tok = om.token_mask(f, s, sink)
+        a = om.kept_tiles(f, s, T, sink)
+        b = om.kept_tiles_bruteforce(tok, T)
+        assert a.shape == b.shape
+        assert np.array_equal(a, b), (f, s, T, sink)
+
+
+def test_csr_csc_consistent():
+    kept = om.kept_tiles(9, 16, 8, True)
+    rp, ci = om.csr(kept)
+    cp, ri = om.csc(kept)
+    assert rp[-1] == cp[-1] == kept.sum()
+    for u in range(kept.shape[0]):
+        cols = ci[rp[u]:rp[u + 1]]
+        assert np.all(np.diff(cols) > 0)
+        assert np.array_equal(cols, np.nonzero(kept[u])[0])
+    for v in range(kept.shape[1]):
+        rows = ri[cp[v]:cp[v + 1]]
+        assert np.array_equal(rows, np.nonzero(kept[:, v])[0])
+
+
+def test_dense_limit_two_frames():
+    # f <= 2: both frame distances are in band 0 with full width, so the
+    # mask is the dense n x n mask (the reduction to plain attention)
+    for s in [1, 5, 64]:
+        assert om.token_mask(2, s, sink=False).all()
+        assert om.token_mask(1, s, sink=False).all()
+
+
+def test_tile_pairs_counts_valid_tokens():
+    f, s, T = 5, 7, 4
+    kept = om.kept_tiles(f, s, T, True)
+    eff = om.effective_mask(f, s, T, True)
+    assert om.tile_pairs(kept, f * s, T) == int(eff.sum())

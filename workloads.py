@@ -1,0 +1,90 @@
+"""Seeded synthetic workloads shared by the tests, smoke() and bench.py.
+
+This module holds shapes and random-number generation only: none of the
+attention or mask arithmetic lives here, so both the GPU path's tests and the
+oracle can draw identical inputs from it without sharing any method code.
+
+The shapes stand in for the video models the radial-attention pages evaluate
+(HunyuanVideo 5 s 720p, Wan2.1-14B 720p, 4x-longer HunyuanVideo, and a
+training step); their latent videos are not available, so Q, K, V (and dO)
+are i.i.d. N(0, 1) draws rounded to bf16.  The work the kernels do depends
+only on the shapes and the mask, never on the values.
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+
+import torch
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    frames: int
+    tokens_per_frame: int
+    D: int
+    T: int
+    seed: int
+    backward: bool = False
+    desc: str = ""
+
+    @property
+    def N(self) -> int:
+        return self.frames * self.tokens_per_frame
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.D)
+
+
+WORKLOADS = {
+    w.name: w
+    for w in [
+        Workload("tiny_f8_s256", 1, 2, 8, 256, 64, 64, 1,
+                 desc="tiny radial attention fwd: 8 frames x 256 tokens, D=64, 64x64 tiles"),
+        Workload("hunyuan_5s_720p", 1, 24, 33, 3600, 128, 128, 2,
+                 desc="HunyuanVideo-shaped 5 s 720p fwd: 33 latent frames x 3600 tokens (80x45)"),
+        Workload("wan21_720p", 1, 40, 21, 3600, 128, 128, 3,
+                 desc="Wan2.1-14B-shaped 720p fwd: 21 latent frames x 3600 tokens"),
+        Workload("hunyuan_4x_long", 1, 24, 129, 3600, 128, 128, 4,
+                 desc="4x longer HunyuanVideo-shaped fwd: 129 latent frames x 3600 tokens"),
+        Workload("train_f66", 1, 24, 66, 3600, 128, 128, 5, backward=True,
+                 desc="training step fwd+bwd: 66 latent frames x 3600 tokens"),
+    ]
+}
+
+ORDER = ["tiny_f8_s256", "hunyuan_5s_720p", "wan21_720p", "hunyuan_4x_long", "train_f66"]
+
+
+def randn_bf16(shape, gen: torch.Generator) -> torch.Tensor:
+    """i.i.d. N(0,1) drawn in float32 on the CPU, rounded to bf16 (RNE)."""
+    return torch.randn(shape, generator=gen, dtype=torch.float32).to(torch.bfloat16)
+
+
+def make_inputs(B: int, H: int, N: int, D: int, seed: int, with_dout: bool = False,
+                heads=None):
+    """Q, K, V (and dO) as CPU bf16 tensors [B, H, N, D], drawn in that order
+    from ``torch.Generator('cpu').manual_seed(seed)``.
+
+    ``heads``: optionally keep only these head indices of the full draw (the
+    draw itself is always the full [B, H, N, D] so values do not depend on
+    which heads are kept).
+    """
+    g = torch.Generator("cpu").manual_seed(seed)
+    names = ["q", "k", "v"] + (["do"] if with_dout else [])
+    out = []
+    for _ in names:
+        t = randn_bf16((B, H, N, D), g)
+        if heads is not None:
+            t = t[:, list(heads)].contiguous()
+        out.append(t)
+    return tuple(out)
+
+
+def workload_inputs(w: Workload, with_dout: bool | None = None, heads=None):
+    wd = w.backward if with_dout is None else with_dout
+    return make_inputs(w.B, w.H, w.N, w.D, w.seed, wd, heads)
