@@ -1,0 +1,172 @@
+/*
+ * radial.h -- C ABI of the radial block-sparse attention library (libradial.so).
+ *
+ * The library computes multi-head softmax attention under the static
+ * "radial" mask of Radial Attention (O(n log n) sparse attention with energy
+ * decay for long video generation), on AMD Instinct MI355X (gfx950) GPUs.
+ *
+ * Sources (abbreviations used below):
+ *   review   -- jaehun.me paper review "Radial Attention: O(n log n) Sparse
+ *               Attention with Energy Decay for Long Video Generation",
+ *               Prompt 1.3.1 (method steps and the f=4, s=9 toy example);
+ *               bracketed names (§3, §4.2, Eq.4, Fig.5) are the paper's own
+ *               numbering as the review quotes it.
+ *   rebuttal -- paperhub.cn author responses for the same paper (ablations
+ *               of the sink, the central band and the band width scale).
+ *
+ * Conventions for every call:
+ *   - Return value: RADIAL_OK (0) or a negative RADIAL_E_* code.  No call
+ *     aborts or throws across the ABI.  radial_last_error() gives a
+ *     human-readable detail string for the calling thread's last failure.
+ *   - Tensors are dense row-major [B, H, N, D] (bf16: the raw 16-bit
+ *     bfloat16 pattern) or [B, H, N] (fp32), owned by the caller, in device
+ *     memory of the current HIP device, 16-byte aligned.  Element (b,h,n,d)
+ *     sits at ((b*H + h)*N + n)*D + d.  Offsets are computed in 64 bits.
+ *   - Compute calls are asynchronous on the given HIP stream (hipStream_t
+ *     passed as void*; NULL = the default stream).  The caller synchronises.
+ *     They never allocate device memory and never synchronise the device.
+ *   - A layout is immutable once built and uploaded; it may be shared by
+ *     any number of streams and threads.  Only radial_layout_upload and
+ *     radial_layout_destroy modify it and must not race with its use.
+ */
+#ifndef RADIAL_H
+#define RADIAL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------ */
+enum {
+  RADIAL_OK = 0,
+  RADIAL_E_INVALID = -1,     /* null / misaligned pointer, bad scalar value   */
+  RADIAL_E_UNSUPPORTED = -2, /* (D, block_size) pair without a compiled kernel */
+  RADIAL_E_SHAPE = -3,       /* N differs from frames * tokens_per_frame       */
+  RADIAL_E_NOMEM = -4,       /* host or device allocation failed               */
+  RADIAL_E_HIP = -5,         /* a HIP runtime call or kernel launch failed     */
+  RADIAL_E_STATE = -6        /* layout not uploaded to the current device      */
+};
+
+/* ---- layout flags ------------------------------------------------------ */
+enum {
+  /* Attention sink: every query may attend every key of frame 0
+     (review Step 4; paper §4.2, Appx A.1 Eq.8).  On in the paper's runs. */
+  RADIAL_SINK = 1u << 0,
+  /* Keep every tile: plain dense attention through the same kernels, the
+     in-library dense baseline. */
+  RADIAL_DENSE = 1u << 1
+};
+
+typedef struct radial_layout radial_layout; /* opaque */
+
+/*
+ * radial_mask_build -- compile the radial mask of a video with `frames`
+ * frames of `tokens_per_frame` tokens (n = frames * tokens_per_frame) into
+ * a block-sparse layout of block_size x block_size tiles.  Host only; no
+ * HIP call is made.
+ *
+ * Token q = i*s + a is position a (row-major in-frame index) of frame i
+ * (review "Terms and variables"; the 4-D mask is flattened as in paper
+ * Eq.4 / §4.2).  Query (i, a) may attend key (j, b) iff
+ *   - RADIAL_SINK is set and j == 0, or
+ *   - with delta = |i - j|, r = floor(log2(max(delta, 1))) (temporal band,
+ *     review Step 2-A, paper §4.2 Fig.5a) and w = floor(s / 2^r) (spatial
+ *     half width, review Step 2-B, paper Fig.5b):
+ *       w >= 1: |a - b| < w (strict, as the review's toy example fixes);
+ *       w == 0: a == b and delta is a multiple of ceil(2^r / s) (diagonal
+ *               subsampling below unit width, review Step 2-C, paper Fig.5
+ *               caption).
+ * A tile (u, v) is kept iff at least one allowed token pair lies in it, and
+ * kept tiles are computed in full (review Step 5, paper §4.2: block-wise
+ * computation in 128 x 128 blocks).  The last tile row/column is partial
+ * when block_size does not divide n.
+ *
+ * frames >= 1, tokens_per_frame >= 1, n < 2^31, 1 <= block_size <= 4096.
+ * flags: RADIAL_SINK | RADIAL_DENSE.  On success *out owns a new layout
+ * (free with radial_layout_destroy); on failure *out is set to NULL.
+ */
+int radial_mask_build(int64_t frames, int64_t tokens_per_frame, int32_t block_size,
+                      uint32_t flags, radial_layout **out);
+
+/* Sizes of a layout.  n_tokens = frames * tokens_per_frame; n_blocks =
+   ceil(n / block_size); nnz_tiles = kept tiles; nnz_pairs = token pairs
+   inside kept tiles, counting only rows and columns < n (the work the
+   kernels do per batch and head).  Any output pointer may be NULL. */
+int radial_layout_info(const radial_layout *L, int64_t *n_tokens, int32_t *n_blocks,
+                       int64_t *nnz_tiles, int64_t *nnz_pairs);
+
+/* Host copies of the tile lists.  CSR: row_ptr[n_blocks + 1] and
+   col_idx[nnz_tiles], key tiles ascending per query tile.  CSC:
+   col_ptr[n_blocks + 1] and row_idx[nnz_tiles], query tiles ascending per
+   key tile.  Any pointer may be NULL (that array is skipped). */
+int radial_layout_export(const radial_layout *L, int32_t *row_ptr, int32_t *col_idx,
+                         int32_t *col_ptr, int32_t *row_idx);
+
+/* Band table, one entry per frame distance delta in [0, frames):
+   band[delta] = r, width[delta] = w, period[delta] = sampling period
+   (1 when w >= 1).  Any pointer may be NULL. */
+int radial_layout_band_table(const radial_layout *L, int32_t *band, int64_t *width,
+                             int64_t *period);
+
+/* Token-level mask for testing: out[q * n + k] = 1 if query q may attend
+   key k, else 0.  Needs cap >= n * n bytes; returns RADIAL_E_INVALID if
+   n * n > cap. */
+int radial_layout_token_mask(const radial_layout *L, uint8_t *out, int64_t cap);
+
+/* Copy the tile lists to the current HIP device (blocking; allocates device
+   memory owned by the layout).  Must be called once before any compute call
+   on that device; a second call on another device moves the layout there. */
+int radial_layout_upload(radial_layout *L);
+
+/* Free a layout and its device copy.  NULL is ignored. */
+void radial_layout_destroy(radial_layout *L);
+
+/*
+ * radial_attn_fwd -- O = softmax(scale * Q K^T + M) V under the layout's
+ * mask M (review Step 0, paper §3 Eq.1/Eq.2), for every batch b and head h.
+ *
+ *   q, k, v : bf16 [B, H, N, D] inputs.
+ *   o       : bf16 [B, H, N, D] output (rounded to nearest even).
+ *   lse     : fp32 [B, H, N] output, natural-log log-sum-exp of the scaled,
+ *             masked logits of each query row (used by the backward pass).
+ * N must equal the layout's n; (D, block_size) must be (64, 64) or
+ * (128, 128); B, H >= 1; scale finite and > 0 (usually 1/sqrt(D)).
+ * Products run on bf16 MFMA with fp32 accumulation and an fp32 online
+ * softmax; the probabilities are rounded to bf16 before the P V product.
+ */
+int radial_attn_fwd(const radial_layout *L, int32_t B, int32_t H, int64_t N, int32_t D,
+                    float scale, const void *q, const void *k, const void *v, void *o,
+                    float *lse, void *hip_stream);
+
+/* Workspace bytes radial_attn_bwd needs for these sizes (fp32 row terms). */
+size_t radial_attn_bwd_workspace_bytes(const radial_layout *L, int32_t B, int32_t H,
+                                       int64_t N, int32_t D);
+
+/*
+ * radial_attn_bwd -- gradients of the forward above for an upstream
+ * gradient dout = dL/dO: dq, dk, dv (bf16 [B, H, N, D], fully overwritten).
+ * o and lse must be the forward's outputs for the same q, k, v, scale and
+ * layout.  The probabilities are recomputed from lse; Delta = rowsum(dO*O)
+ * is formed first in `workspace` (caller-owned device memory of at least
+ * radial_attn_bwd_workspace_bytes bytes, 16-byte aligned).  Deterministic:
+ * no atomics, fixed summation order.
+ */
+int radial_attn_bwd(const radial_layout *L, int32_t B, int32_t H, int64_t N, int32_t D,
+                    float scale, const void *q, const void *k, const void *v, const void *o,
+                    const float *lse, const void *dout, void *dq, void *dk, void *dv,
+                    void *workspace, size_t workspace_bytes, void *hip_stream);
+
+/* Static text for a status code. */
+const char *radial_status_string(int status);
+
+/* Detail of the calling thread's last failed call ("" if none). */
+const char *radial_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RADIAL_H */

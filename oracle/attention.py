@@ -117,3 +117,18 @@ def bwd_masked(q, k, v, do, mask, scale):
     delta = (p * dp).sum(axis=1, keepdims=True)
     ds = p * (dp - delta)
     return scale * (ds @ k), scale * (ds.T @ q), p.T @ do
+
+
+def bwd_dq_tile(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray,
+                kept: np.ndarray, T: int, scale: float, u: int) -> np.ndarray:
+    """dQ for the valid rows of query tile u only (same formulas as ``bwd``,
+    restricted to one row block: a query row's gradient depends only on its
+    own softmax row)."""
+    n = q.shape[0]
+    rows = slice(u * T, min(n, (u + 1) * T))
+    cols = tile_columns(kept[u], n, T)
+    z = scale * (q[rows] @ k[cols].T)
+    p, _ = _softmax_rows(z)
+    dp = do[rows] @ v[cols].T
+    delta = (p * dp).sum(axis=1, keepdims=True)
+    return scale * ((p * (dp - delta)) @ k[cols])

@@ -1,0 +1,207 @@
+"""Radial block-sparse attention on AMD MI355X (gfx950).
+
+Thin Python binding of ``libradial.so`` (C ABI declared in include/radial.h).
+The binding only marshals arguments: every step of the mask compilation and
+of the attention runs in the library.  torch provides device memory and the
+current HIP stream.
+
+    L = Layout(frames=33, tokens_per_frame=3600, block_size=128)  # sink on
+    o, lse = attn_fwd(q, k, v, L)             # q, k, v: bf16 [B, H, N, D] on GPU
+    dq, dk, dv = attn_bwd(q, k, v, o, lse, do, L)
+
+Raises RuntimeError when the library is not built (there is no fallback).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import numpy as np
+
+__all__ = ["Layout", "attn_fwd", "attn_bwd", "lib", "LIB_PATH", "SINK", "DENSE",
+           "RadialError"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libradial.so")
+
+SINK = 1
+DENSE = 2
+
+_STATUS = {0: "RADIAL_OK", -1: "RADIAL_E_INVALID", -2: "RADIAL_E_UNSUPPORTED",
+           -3: "RADIAL_E_SHAPE", -4: "RADIAL_E_NOMEM", -5: "RADIAL_E_HIP", -6: "RADIAL_E_STATE"}
+
+_lib = None
+
+
+class RadialError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {detail}")
+        self.status = status
+
+
+def _declare(L):
+    c = ctypes
+    vp, i32, i64, u32, f32, sz = c.c_void_p, c.c_int32, c.c_int64, c.c_uint32, c.c_float, c.c_size_t
+    P = c.POINTER
+    sigs = {
+        "radial_mask_build": (c.c_int, [i64, i64, i32, u32, P(vp)]),
+        "radial_layout_info": (c.c_int, [vp, P(i64), P(i32), P(i64), P(i64)]),
+        "radial_layout_export": (c.c_int, [vp, vp, vp, vp, vp]),
+        "radial_layout_band_table": (c.c_int, [vp, vp, vp, vp]),
+        "radial_layout_token_mask": (c.c_int, [vp, vp, i64]),
+        "radial_layout_upload": (c.c_int, [vp]),
+        "radial_layout_destroy": (None, [vp]),
+        "radial_attn_fwd": (c.c_int, [vp, i32, i32, i64, i32, f32, vp, vp, vp, vp, vp, vp]),
+        "radial_attn_bwd_workspace_bytes": (sz, [vp, i32, i32, i64, i32]),
+        "radial_attn_bwd": (c.c_int, [vp, i32, i32, i64, i32, f32, vp, vp, vp, vp, vp, vp,
+                                      vp, vp, vp, vp, sz, vp]),
+        "radial_status_string": (c.c_char_p, [c.c_int]),
+        "radial_last_error": (c.c_char_p, []),
+    }
+    for name, (res, args) in sigs.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+
+
+def lib():
+    """The loaded library (loaded once).  RuntimeError if it is not built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run `python -m static_block_sparse_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        _declare(L)
+        _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != 0:
+        raise RadialError(status, lib().radial_last_error().decode())
+
+
+class Layout:
+    """Block-sparse layout of the radial mask (owns a ``radial_layout``)."""
+
+    def __init__(self, frames: int, tokens_per_frame: int, block_size: int = 128,
+                 sink: bool = True, dense: bool = False):
+        flags = (SINK if sink else 0) | (DENSE if dense else 0)
+        h = ctypes.c_void_p()
+        _check(lib().radial_mask_build(frames, tokens_per_frame, block_size, flags, ctypes.byref(h)))
+        self._h = h
+        self.frames = frames
+        self.tokens_per_frame = tokens_per_frame
+        self.block_size = block_size
+        self.sink = sink
+        self.dense = dense
+        n, nb, nz, pairs = ctypes.c_int64(), ctypes.c_int32(), ctypes.c_int64(), ctypes.c_int64()
+        _check(lib().radial_layout_info(h, ctypes.byref(n), ctypes.byref(nb), ctypes.byref(nz),
+                                        ctypes.byref(pairs)))
+        self.n = n.value
+        self.n_blocks = nb.value
+        self.nnz_tiles = nz.value
+        self.nnz_pairs = pairs.value
+        self._device = None
+
+    @property
+    def handle(self):
+        return self._h
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and _lib is not None:
+            _lib.radial_layout_destroy(h)
+            self._h = None
+
+    def csr(self):
+        rp = np.empty(self.n_blocks + 1, dtype=np.int32)
+        ci = np.empty(self.nnz_tiles, dtype=np.int32)
+        _check(lib().radial_layout_export(self._h, rp.ctypes.data, ci.ctypes.data, None, None))
+        return rp, ci
+
+    def csc(self):
+        cp = np.empty(self.n_blocks + 1, dtype=np.int32)
+        ri = np.empty(self.nnz_tiles, dtype=np.int32)
+        _check(lib().radial_layout_export(self._h, None, None, cp.ctypes.data, ri.ctypes.data))
+        return cp, ri
+
+    def band_table(self):
+        r = np.empty(self.frames, dtype=np.int32)
+        w = np.empty(self.frames, dtype=np.int64)
+        p = np.empty(self.frames, dtype=np.int64)
+        _check(lib().radial_layout_band_table(self._h, r.ctypes.data, w.ctypes.data, p.ctypes.data))
+        return r, w, p
+
+    def token_mask(self):
+        out = np.empty((self.n, self.n), dtype=np.uint8)
+        _check(lib().radial_layout_token_mask(self._h, out.ctypes.data, out.size))
+        return out.astype(bool)
+
+    def upload(self, device=None):
+        """Copy the tile lists to a GPU (the current one by default)."""
+        import torch
+        dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+        if self._device != dev:
+            with torch.cuda.device(dev):
+                _check(lib().radial_layout_upload(self._h))
+            self._device = dev
+        return self
+
+
+def _check_qkv(name, t, ref=None):
+    import torch
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype != torch.bfloat16:
+        raise ValueError(f"{name} must be bfloat16")
+    if t.dim() != 4:
+        raise ValueError(f"{name} must be [B, H, N, D]")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ref is not None and (t.shape != ref.shape or t.device != ref.device):
+        raise ValueError(f"{name} must match q in shape and device")
+
+
+def attn_fwd(q, k, v, layout: Layout, scale: float | None = None, out=None, lse=None):
+    """Radial attention forward.  Returns (o bf16 [B,H,N,D], lse fp32 [B,H,N])."""
+    import torch
+    _check_qkv("q", q)
+    _check_qkv("k", k, q)
+    _check_qkv("v", v, q)
+    B, H, N, D = q.shape
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    o = torch.empty_like(q) if out is None else out
+    l = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    layout.upload(q.device)
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        _check(lib().radial_attn_fwd(layout.handle, B, H, N, D, scale, q.data_ptr(), k.data_ptr(),
+                                     v.data_ptr(), o.data_ptr(), l.data_ptr(), stream))
+    return o, l
+
+
+def attn_bwd(q, k, v, o, lse, do, layout: Layout, scale: float | None = None,
+             workspace=None):
+    """Radial attention backward.  Returns (dq, dk, dv), bf16 [B,H,N,D]."""
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
+        _check_qkv(name, t, None if name == "q" else q)
+    B, H, N, D = q.shape
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N) or not lse.is_contiguous():
+        raise ValueError("lse must be contiguous fp32 [B, H, N]")
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    need = lib().radial_attn_bwd_workspace_bytes(layout.handle, B, H, N, D)
+    ws = workspace
+    if ws is None or ws.numel() * ws.element_size() < need:
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    layout.upload(q.device)
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        _check(lib().radial_attn_bwd(layout.handle, B, H, N, D, scale, q.data_ptr(), k.data_ptr(),
+                                     v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
+                                     dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws.data_ptr(),
+                                     ws.numel() * ws.element_size(), stream))
+    return dq, dk, dv

@@ -1,0 +1,70 @@
+"""Builds libradial.so in-tree with hipcc for gfx950.
+
+    python -m static_block_sparse_amd.build      (from the repository root)
+
+Every source is compiled on each call (the build is a few tens of seconds).
+"""
+
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+import tempfile
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(PKG, "libradial.so")
+
+SOURCES = ["mask.cpp", "capi.cpp", "attn_fwd.hip", "attn_bwd.hip"]
+ARCH = "gfx950"
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+COMMON = ["-O3", "-std=c++17", "-fPIC", "-I", INCLUDE, "-I", CSRC, "-Wall"]
+# packed fp32 instructions off for device code (a flag of the device pass;
+# the host pass warns that it does not know it, which is harmless)
+DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+
+
+def _run(cmd):
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    out = "\n".join(l for l in r.stdout.splitlines()
+                    if "not a recognized feature for this target" not in l)
+    if r.returncode != 0:
+        raise RuntimeError(f"build step failed ({r.returncode}): {' '.join(cmd)}\n{out}")
+    return out
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source and link libradial.so; returns its path."""
+    if not os.path.exists(HIPCC):
+        raise RuntimeError(f"hipcc not found at {HIPCC}")
+    tmp = tempfile.mkdtemp(prefix="radial_build_")
+    try:
+        objs = []
+        for src in SOURCES:
+            obj = os.path.join(tmp, src + ".o")
+            path = os.path.join(CSRC, src)
+            if src.endswith(".hip"):
+                cmd = [HIPCC, "-x", "hip", *DEVICE, *COMMON, "-c", path, "-o", obj]
+            else:
+                cmd = [HIPCC, *COMMON, "-D__HIP_PLATFORM_AMD__", "-c", path, "-o", obj]
+            out = _run(cmd)
+            if verbose and out.strip():
+                print(out)
+            objs.append(obj)
+        tmp_lib = os.path.join(tmp, "libradial.so")
+        _run([HIPCC, *DEVICE, "-shared", "-fPIC", "-o", tmp_lib, *objs])
+        shutil.copyfile(tmp_lib, LIB + ".tmp")
+        os.replace(LIB + ".tmp", LIB)
+    finally:
+        shutil.rmtree(tmp, ignore_errors=True)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,146 @@
+// Device-side helpers shared by the radial attention kernels (gfx950).
+//
+// MFMA conventions used throughout (v_mfma_f32_32x32x16_bf16, wave64):
+//   * lane l has column c = l % 32 and k-group g = l / 32;
+//   * A operand (32 x 16, M x K): lane l holds row c, 8 bf16 along K;
+//   * B operand (16 x 32, K x N): lane l holds column c, 8 bf16 along K;
+//   * C/D (32 x 32 fp32): lane l holds column c, register r is row
+//     8 * (r / 4) + 4 * g + (r % 4).
+// The product sums over K, so any one-to-one assignment of the 16 K indices
+// to (g, element) gives the same result as long as A and B use the same
+// assignment.  The kernels pick, per 16-wide K step,
+//   element e of k-group g  <->  k = 8 * (e / 4) + 4 * g + (e % 4),
+// which is exactly the row set a C fragment's registers 0..7 (or 8..15,
+// shifted by 16) hold.  That lets an fp32 C fragment be rounded to bf16 and
+// fed back as an A or B operand without moving data between lanes: the
+// fragment's column index stays the lane's column and its rows become the
+// contraction index.  Operands loaded from memory with that assignment read
+// two runs of 4 consecutive elements: [4g, 4g+4) and [8+4g, 8+4g+4).
+// Operands whose K index is contiguous in memory (the head dimension D of
+// Q, K, V, dO rows) use the plain assignment k = 8 * g + e instead; both
+// operands of such a product are loaded that way.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace radial {
+
+typedef __bf16 bf16;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ f32x16 zero16() {
+  f32x16 z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.f;
+  return z;
+}
+
+__device__ __forceinline__ bf16x8 zero_bf16x8() {
+  bf16x8 z;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) z[i] = bf16(0.f);
+  return z;
+}
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 cat(bf16x4 lo, bf16x4 hi) {
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// 8 bf16 from the permuted K assignment: p[0..3] and p[8..11].
+__device__ __forceinline__ bf16x8 ld_perm(const bf16 *p) {
+  return cat(*reinterpret_cast<const bf16x4 *>(p), *reinterpret_cast<const bf16x4 *>(p + 8));
+}
+
+__device__ __forceinline__ bf16x8 ld8(const bf16 *p) {
+  return *reinterpret_cast<const bf16x8 *>(p);
+}
+
+__device__ __forceinline__ void st8(bf16 *p, bf16x8 v) {
+  *reinterpret_cast<bf16x8 *>(p) = v;
+}
+
+__device__ __forceinline__ void st4(bf16 *p, bf16x4 v) {
+  *reinterpret_cast<bf16x4 *>(p) = v;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Work-item remap so that each XCD (of 8) processes one contiguous range
+// of work items: the hardware hands consecutive workgroups to XCDs round
+// robin, so workgroup b runs on XCD b % 8.  Bijective on [0, n).
+__device__ __forceinline__ int xcd_remap(int b, int n) {
+  constexpr int X = 8;
+  const int q = n / X, r = n % X;
+  const int x = b % X, k = b / X;
+  return (x < r) ? x * (q + 1) + k : r * (q + 1) + (x - r) * q + k;
+}
+
+// Rows [0, ROWS) x cols [0, D) of a row-major bf16 tile into LDS with row
+// stride LS (elements); rows at or beyond `valid` are zero-filled.
+template <int ROWS, int D, int LS, int NT>
+__device__ __forceinline__ void load_rows(bf16 *lds, const bf16 *g, int valid, int tid) {
+  constexpr int CH = D / 8;           // 16-byte chunks per row
+  constexpr int TOT = ROWS * CH;
+  static_assert(TOT % NT == 0, "tile chunks must divide the thread count");
+  bf16x8 buf[TOT / NT];
+#pragma unroll
+  for (int it = 0; it < TOT / NT; ++it) {
+    const int c = tid + it * NT;
+    const int row = c / CH, ch = c % CH;
+    buf[it] = row < valid ? ld8(g + (int64_t)row * D + ch * 8) : zero_bf16x8();
+  }
+#pragma unroll
+  for (int it = 0; it < TOT / NT; ++it) {
+    const int c = tid + it * NT;
+    const int row = c / CH, ch = c % CH;
+    st8(lds + row * LS + ch * 8, buf[it]);
+  }
+}
+
+// Same tile stored transposed: lds[d * LS + row].  Each thread moves a
+// 4-row x 8-column block; consecutive threads take consecutive row groups so
+// the 8-byte LDS stores of a wave are contiguous.
+template <int ROWS, int D, int LS, int NT>
+__device__ __forceinline__ void load_rows_t(bf16 *lds, const bf16 *g, int valid, int tid) {
+  constexpr int RG = ROWS / 4;        // row groups
+  constexpr int TOT = RG * (D / 8);
+  static_assert(TOT % NT == 0, "tile blocks must divide the thread count");
+  bf16x8 buf[TOT / NT][4];
+#pragma unroll
+  for (int it = 0; it < TOT / NT; ++it) {
+    const int c = tid + it * NT;
+    const int rg = c % RG, ch = c / RG;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = rg * 4 + r;
+      buf[it][r] = row < valid ? ld8(g + (int64_t)row * D + ch * 8) : zero_bf16x8();
+    }
+  }
+#pragma unroll
+  for (int it = 0; it < TOT / NT; ++it) {
+    const int c = tid + it * NT;
+    const int rg = c % RG, ch = c / RG;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      bf16x4 col;
+      col[0] = buf[it][0][e];
+      col[1] = buf[it][1][e];
+      col[2] = buf[it][2][e];
+      col[3] = buf[it][3][e];
+      st4(lds + (ch * 8 + e) * LS + rg * 4, col);
+    }
+  }
+}
+
+}  // namespace radial

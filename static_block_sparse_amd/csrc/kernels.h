@@ -1,0 +1,34 @@
+// Host-side launchers of the radial attention kernels (internal).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace radial {
+
+struct FwdArgs {
+  const void *q, *k, *v;
+  void *o;
+  float *lse;
+  const int32_t *row_ptr, *col_idx;  // device CSR of the layout
+  int32_t BH, N, D, T, nb;
+  float scale;
+};
+
+struct BwdArgs {
+  const void *q, *k, *v, *o, *dout;
+  const float *lse;
+  void *dq, *dk, *dv;
+  float *delta;                      // workspace, fp32 [BH, N]
+  const int32_t *row_ptr, *col_idx;  // CSR (dQ pass)
+  const int32_t *col_ptr, *row_idx;  // CSC (dK/dV pass)
+  const int32_t *col_order;          // key tiles, longest column first
+  int32_t BH, N, D, T, nb;
+  float scale;
+};
+
+// Both return hipErrorInvalidValue for an unsupported (D, T) pair.
+hipError_t launch_fwd(const FwdArgs &a, hipStream_t stream);
+hipError_t launch_bwd(const BwdArgs &a, hipStream_t stream);
+
+}  // namespace radial

@@ -1,0 +1,46 @@
+// Internal definition of the radial layout (host arrays + device copy).
+#pragma once
+
+#include <cstdint>
+#include <string>
+#include <vector>
+
+struct radial_layout {
+  int64_t frames = 0;
+  int64_t tokens_per_frame = 0;
+  int64_t n = 0;           // frames * tokens_per_frame
+  int32_t block = 0;       // tile edge T
+  uint32_t flags = 0;
+  int32_t nb = 0;          // ceil(n / T)
+  int64_t nnz_tiles = 0;
+  int64_t nnz_pairs = 0;
+
+  std::vector<int32_t> band_r;      // per frame distance
+  std::vector<int64_t> band_w;
+  std::vector<int64_t> band_period;
+
+  std::vector<int32_t> row_ptr, col_idx;  // CSR: key tiles per query tile
+  std::vector<int32_t> col_ptr, row_idx;  // CSC: query tiles per key tile
+  std::vector<int32_t> col_order;         // key tiles, longest column first
+
+  // device copy (one allocation): row_ptr | col_idx | col_ptr | row_idx | col_order
+  int device = -1;
+  void *d_base = nullptr;
+  const int32_t *d_row_ptr = nullptr;
+  const int32_t *d_col_idx = nullptr;
+  const int32_t *d_col_ptr = nullptr;
+  const int32_t *d_row_idx = nullptr;
+  const int32_t *d_col_order = nullptr;
+};
+
+namespace radial {
+
+// Fills everything above except the device copy.  Returns an empty string
+// on success, else a description of what was invalid.
+std::string build_layout(int64_t frames, int64_t tokens_per_frame, int32_t block,
+                         uint32_t flags, radial_layout &L);
+
+// Token predicate of the layout's mask (tests only).
+bool token_allowed(const radial_layout &L, int64_t q, int64_t k);
+
+}  // namespace radial

@@ -1,0 +1,187 @@
+// Radial mask compiler: (frames, tokens per frame, tile edge, flags) ->
+// block-sparse tile lists (CSR for the forward and dQ passes, CSC for the
+// dK/dV pass).
+//
+// Mask definition (jaehun.me review "Radial Attention: O(n log n) Sparse
+// Attention with Energy Decay for Long Video Generation", Prompt 1.3.1):
+//   * temporal band of a frame pair at distance delta:
+//       r = floor(log2(max(delta, 1)))           (Step 2-A; paper §4.2 Fig.5a)
+//   * spatial half width kept inside that frame pair:
+//       w = floor(s / 2^r)                        (Step 2-B; paper Fig.5b)
+//     and a key at in-frame position b is reachable from position a iff
+//     |a - b| < w (strict edge, as the toy example with s = 9, w = 4 admits
+//     positions 1..7 around the centre 4);
+//   * below unit width (w == 0) only the diagonal b == a is kept, and only
+//     for frame pairs whose distance is a multiple of ceil(2^r / s), which
+//     keeps the band's amortised density near 2^-r (Step 2-C; paper Fig.5
+//     caption);
+//   * attention sink: all of frame 0 is reachable (Step 4; paper Eq.8);
+//   * tiles: a T x T tile is kept iff it holds at least one allowed pair,
+//     and kept tiles are computed in full (Step 5; paper §4.2).
+//
+// Construction: for one query tile, its rows fall into one or more frame
+// segments (frame i, positions a0..a1).  Against key frame j the keys
+// reachable from a whole segment form a single position run
+// [a0 - w + 1, a1 + w - 1] clipped to the frame (runs of consecutive query
+// positions overlap because every run is at least one key wide), or
+// [a0, a1] on the sampled diagonal, or the whole frame for the sink.  Each
+// run maps to a run of key tiles; the union of the runs of a query tile,
+// sorted and merged, is its CSR row.
+#include <algorithm>
+#include <cstdint>
+#include <string>
+#include <utility>
+#include <vector>
+
+#include "layout.h"
+#include "radial.h"
+
+namespace radial {
+namespace {
+
+inline int bit_length(uint64_t x) { return x == 0 ? 0 : 64 - __builtin_clzll(x); }
+
+struct Band {
+  int32_t r;
+  int64_t w;
+  int64_t period;
+};
+
+inline Band band_of(int64_t delta, int64_t s) {
+  Band b;
+  b.r = bit_length(static_cast<uint64_t>(delta < 1 ? 1 : delta)) - 1;
+  b.w = (b.r >= 63) ? 0 : (s >> b.r);
+  if (b.w >= 1) {
+    b.period = 1;
+  } else {
+    const int64_t p2 = int64_t(1) << b.r;  // r <= 62 here since delta < 2^63
+    b.period = (p2 + s - 1) / s;
+  }
+  return b;
+}
+
+}  // namespace
+
+std::string build_layout(int64_t frames, int64_t s, int32_t T, uint32_t flags,
+                         radial_layout &L) {
+  if (frames < 1) return "frames must be >= 1";
+  if (s < 1) return "tokens_per_frame must be >= 1";
+  if (T < 1 || T > 4096) return "block_size must be in [1, 4096]";
+  if (flags & ~uint32_t(RADIAL_SINK | RADIAL_DENSE)) return "unknown flag bits";
+  if (frames > (int64_t(1) << 31) / s) return "frames * tokens_per_frame must be < 2^31";
+  const int64_t n = frames * s;
+  if (n >= (int64_t(1) << 31)) return "frames * tokens_per_frame must be < 2^31";
+  const bool sink = flags & RADIAL_SINK;
+  const bool dense = flags & RADIAL_DENSE;
+
+  L.frames = frames;
+  L.tokens_per_frame = s;
+  L.n = n;
+  L.block = T;
+  L.flags = flags;
+  const int64_t nb = (n + T - 1) / T;
+  L.nb = static_cast<int32_t>(nb);
+
+  L.band_r.resize(frames);
+  L.band_w.resize(frames);
+  L.band_period.resize(frames);
+  for (int64_t d = 0; d < frames; ++d) {
+    const Band b = band_of(d, s);
+    L.band_r[d] = b.r;
+    L.band_w[d] = b.w;
+    L.band_period[d] = b.period;
+  }
+
+  L.row_ptr.assign(nb + 1, 0);
+  L.col_idx.clear();
+  std::vector<std::pair<int64_t, int64_t>> runs;
+  for (int64_t u = 0; u < nb; ++u) {
+    const int64_t q0 = u * T;
+    const int64_t q1 = std::min(n, q0 + T) - 1;
+    if (dense) {
+      for (int64_t v = 0; v < nb; ++v) L.col_idx.push_back(static_cast<int32_t>(v));
+      L.row_ptr[u + 1] = static_cast<int32_t>(L.col_idx.size());
+      continue;
+    }
+    runs.clear();
+    for (int64_t i = q0 / s; i <= q1 / s; ++i) {
+      const int64_t a0 = (i == q0 / s) ? q0 % s : 0;
+      const int64_t a1 = (i == q1 / s) ? q1 % s : s - 1;
+      for (int64_t j = 0; j < frames; ++j) {
+        int64_t lo, hi;
+        if (sink && j == 0) {
+          lo = 0;
+          hi = s - 1;
+        } else {
+          const int64_t delta = i > j ? i - j : j - i;
+          const int64_t w = L.band_w[delta];
+          if (w >= 1) {
+            lo = std::max<int64_t>(0, a0 - w + 1);
+            hi = std::min<int64_t>(s - 1, a1 + w - 1);
+          } else if (delta % L.band_period[delta] == 0) {
+            lo = a0;
+            hi = a1;
+          } else {
+            continue;
+          }
+        }
+        runs.emplace_back((j * s + lo) / T, (j * s + hi) / T);
+      }
+    }
+    std::sort(runs.begin(), runs.end());
+    int64_t next = -1;  // first key tile not yet emitted
+    for (const auto &rv : runs) {
+      for (int64_t v = std::max(rv.first, next); v <= rv.second; ++v)
+        L.col_idx.push_back(static_cast<int32_t>(v));
+      next = std::max(next, rv.second + 1);
+    }
+    L.row_ptr[u + 1] = static_cast<int32_t>(L.col_idx.size());
+  }
+  L.nnz_tiles = static_cast<int64_t>(L.col_idx.size());
+  if (L.nnz_tiles >= (int64_t(1) << 31)) return "too many tiles for 32-bit indices";
+
+  // transpose to CSC (query tiles ascending within each key tile)
+  L.col_ptr.assign(nb + 1, 0);
+  for (int32_t v : L.col_idx) L.col_ptr[v + 1]++;
+  for (int64_t v = 0; v < nb; ++v) L.col_ptr[v + 1] += L.col_ptr[v];
+  L.row_idx.assign(L.nnz_tiles, 0);
+  {
+    std::vector<int32_t> fill(L.col_ptr.begin(), L.col_ptr.end() - 1);
+    for (int64_t u = 0; u < nb; ++u)
+      for (int32_t t = L.row_ptr[u]; t < L.row_ptr[u + 1]; ++t)
+        L.row_idx[fill[L.col_idx[t]]++] = static_cast<int32_t>(u);
+  }
+
+  // longest columns first for the dK/dV pass (the sink columns of frame 0
+  // hold every query tile); ties keep ascending tile order
+  L.col_order.resize(nb);
+  for (int64_t v = 0; v < nb; ++v) L.col_order[v] = static_cast<int32_t>(v);
+  std::stable_sort(L.col_order.begin(), L.col_order.end(), [&](int32_t a, int32_t b) {
+    return (L.col_ptr[a + 1] - L.col_ptr[a]) > (L.col_ptr[b + 1] - L.col_ptr[b]);
+  });
+
+  // valid token pairs inside kept tiles
+  int64_t pairs = 0;
+  for (int64_t u = 0; u < nb; ++u) {
+    const int64_t rows = std::min<int64_t>(T, n - u * T);
+    int64_t cols = 0;
+    for (int32_t t = L.row_ptr[u]; t < L.row_ptr[u + 1]; ++t)
+      cols += std::min<int64_t>(T, n - int64_t(L.col_idx[t]) * T);
+    pairs += rows * cols;
+  }
+  L.nnz_pairs = pairs;
+  return std::string();
+}
+
+bool token_allowed(const radial_layout &L, int64_t q, int64_t k) {
+  const int64_t s = L.tokens_per_frame;
+  if (L.flags & RADIAL_DENSE) return true;
+  const int64_t i = q / s, a = q % s, j = k / s, b = k % s;
+  if ((L.flags & RADIAL_SINK) && j == 0) return true;
+  const int64_t delta = i > j ? i - j : j - i;
+  const int64_t w = L.band_w[delta];
+  if (w >= 1) return (a > b ? a - b : b - a) < w;
+  return a == b && delta % L.band_period[delta] == 0;
+}
+
+}  // namespace radial

@@ -1,0 +1,163 @@
+"""Host-side tests of libradial.so (no GPU needed).
+
+* the library loads and exports every function include/radial.h declares;
+* the C++ mask compiler matches the oracle bit-exactly (CSR, CSC, band
+  table, token mask, pair count), live on small shapes and through stored
+  oracle digests at the full workload shapes;
+* argument validation and the allocation-failure hook return the documented
+  status codes without touching a GPU.
+"""
+
+import ctypes
+import hashlib
+import json
+import os
+import re
+
+import numpy as np
+import pytest
+
+import static_block_sparse_amd as sba
+from oracle import mask as om
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "radial.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(radial_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = sba.lib()
+    names = _declared_functions()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(lib, n), n
+    # and nm agrees that they are exported C symbols (no C++ mangling)
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", sba.LIB_PATH], capture_output=True,
+                         text=True).stdout
+    exported = set(re.findall(r"\bT (radial_\w+)", out))
+    assert set(names) <= exported
+
+
+SMALL = [(4, 9, 4), (8, 256, 64), (5, 7, 3), (33, 3, 16), (12, 1, 4), (6, 100, 64),
+         (3, 50, 128), (40, 2, 7), (20, 33, 32), (66, 256, 128), (17, 100, 64), (1, 5, 2),
+         (2, 300, 128), (9, 130, 128)]
+
+
+@pytest.mark.parametrize("sink", [True, False])
+def test_tiles_match_oracle_small(sink):
+    for f, s, T in SMALL:
+        L = sba.Layout(f, s, T, sink=sink)
+        kept = om.kept_tiles(f, s, T, sink)
+        rp, ci = om.csr(kept)
+        cp, ri = om.csc(kept)
+        grp, gci = L.csr()
+        gcp, gri = L.csc()
+        assert L.n_blocks == kept.shape[0]
+        assert L.nnz_tiles == int(kept.sum())
+        assert np.array_equal(grp, rp) and np.array_equal(gci, ci), (f, s, T)
+        assert np.array_equal(gcp, cp) and np.array_equal(gri, ri), (f, s, T)
+        assert L.nnz_pairs == om.tile_pairs(kept, f * s, T)
+
+
+def test_band_table_matches_oracle():
+    for f, s in [(129, 3600), (600, 3), (40, 1), (8, 256)]:
+        r, w, p = sba.Layout(f, s, 16).band_table()
+        tab = om.band_table(f, s)
+        assert np.array_equal(r, tab[:, 0]) and np.array_equal(w, tab[:, 1])
+        assert np.array_equal(p, tab[:, 2])
+
+
+@pytest.mark.parametrize("sink", [True, False])
+def test_token_mask_matches_oracle(sink):
+    for f, s in [(4, 9), (12, 1), (9, 16), (33, 3), (7, 40)]:
+        got = sba.Layout(f, s, 8, sink=sink).token_mask()
+        assert np.array_equal(got, om.token_mask(f, s, sink)), (f, s)
+
+
+def _digest(a):
+    return hashlib.sha256(np.ascontiguousarray(a, dtype="<i4").tobytes()).hexdigest()
+
+
+def test_tiles_match_oracle_digests_full_size():
+    gold = json.load(open(os.path.join(ROOT, "tests", "golden", "layouts.json")))
+    for g in gold:
+        L = sba.Layout(g["frames"], g["tokens_per_frame"], g["tile"], sink=g["sink"])
+        assert L.n_blocks == g["n_blocks"] and L.nnz_tiles == g["nnz_tiles"]
+        assert L.nnz_pairs == g["nnz_pairs"]
+        rp, ci = L.csr()
+        cp, ri = L.csc()
+        assert _digest(rp) == g["row_ptr"] and _digest(ci) == g["col_idx"], g
+        assert _digest(cp) == g["col_ptr"] and _digest(ri) == g["row_idx"], g
+
+
+def test_dense_flag_keeps_every_tile():
+    L = sba.Layout(7, 50, 32, dense=True)
+    nb = L.n_blocks
+    assert L.nnz_tiles == nb * nb
+    assert L.nnz_pairs == L.n * L.n
+    assert L.token_mask().all()
+
+
+def test_sink_flag_off_by_request():
+    a, b = sba.Layout(33, 3600, 128, sink=True), sba.Layout(33, 3600, 128, sink=False)
+    assert a.nnz_tiles == 389411 and b.nnz_tiles == 371557
+
+
+@pytest.mark.parametrize("args", [(0, 10, 8, 1), (4, 0, 8, 1), (4, 10, 0, 1), (4, 10, 5000, 1),
+                                  (4, 10, 8, 8), (1 << 20, 1 << 12, 128, 1)])
+def test_build_rejects_bad_arguments(args):
+    h = ctypes.c_void_p(123)
+    st = sba.lib().radial_mask_build(*args, ctypes.byref(h))
+    assert st == -1
+    assert h.value is None
+    assert sba.lib().radial_last_error().decode()
+
+
+def test_compute_calls_validate_before_touching_the_gpu():
+    lib = sba.lib()
+    L = sba.Layout(8, 256, 64)
+    dummy = 4096  # 16-byte aligned fake address, never dereferenced
+    args = lambda Lh, B, H, N, D, sc: (Lh, B, H, N, D, sc, dummy, dummy, dummy, dummy, dummy, None)
+    assert lib.radial_attn_fwd(*args(None, 1, 1, 2048, 64, 0.125)) == -1
+    assert lib.radial_attn_fwd(*args(L.handle, 0, 1, 2048, 64, 0.125)) == -1
+    assert lib.radial_attn_fwd(*args(L.handle, 1, 1, 2047, 64, 0.125)) == -3
+    assert lib.radial_attn_fwd(*args(L.handle, 1, 1, 2048, 128, 0.125)) == -2
+    assert lib.radial_attn_fwd(*args(L.handle, 1, 1, 2048, 64, -1.0)) == -1
+    assert lib.radial_attn_fwd(*args(L.handle, 1, 1, 2048, 64, float("nan"))) == -1
+    # valid shapes but the layout was never uploaded
+    assert lib.radial_attn_fwd(*args(L.handle, 1, 1, 2048, 64, 0.125)) == -6
+    assert "upload" in lib.radial_last_error().decode()
+    ws = lib.radial_attn_bwd_workspace_bytes(L.handle, 2, 3, 2048, 64)
+    assert ws >= 2 * 3 * 2048 * 4 and ws % 256 == 0
+    b = (L.handle, 1, 1, 2048, 64, 0.125) + (dummy,) * 10 + (ws, None)
+    assert lib.radial_attn_bwd(*b) == -6
+    b = (L.handle, 1, 1, 2000, 64, 0.125) + (dummy,) * 10 + (ws, None)
+    assert lib.radial_attn_bwd(*b) == -3
+    assert lib.radial_status_string(-3) == b"shape mismatch"
+
+
+def test_allocation_failure_hook(monkeypatch):
+    monkeypatch.setenv("RADIAL_TEST_FAIL_ALLOC", "1")
+    h = ctypes.c_void_p()
+    assert sba.lib().radial_mask_build(8, 256, 64, 1, ctypes.byref(h)) == -4
+    assert h.value is None
+    monkeypatch.setenv("RADIAL_TEST_FAIL_ALLOC", "0")
+    assert sba.lib().radial_mask_build(8, 256, 64, 1, ctypes.byref(h)) == 0
+    sba.lib().radial_layout_destroy(h)
+
+
+def test_layout_is_o_n_log_n_at_tile_level_for_long_videos():
+    # tile density falls as frames grow at fixed s (the radial mask's whole
+    # point); at f = 2 every tile is kept
+    dens = []
+    for f in [2, 8, 32, 128]:
+        L = sba.Layout(f, 3600, 128)
+        dens.append(L.nnz_tiles / L.n_blocks ** 2)
+    assert dens[0] == 1.0
+    assert all(a > b for a, b in zip(dens, dens[1:]))

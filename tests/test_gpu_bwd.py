@@ -1,0 +1,117 @@
+"""GPU parity of the backward pass against the oracle (needs an MI355X).
+
+Small shapes: dQ, dK, dV compared element by element over every head.
+Full-size training workload (66 frames x 3600 tokens, 24 heads): dQ on
+sampled query tiles against the oracle, and dK, dV through identities that
+hold at any size: sum_n dV[n] = sum_m dO[m] (softmax rows sum to one) and
+sum_n dK[n] = 0 (each row of dS sums to zero).
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import static_block_sparse_amd as sba
+import workloads
+from gpu_util import check_close, f64, sample_tiles
+from oracle import attention as oa
+from oracle import mask as om
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+@pytest.mark.parametrize("f,s,T,D,B,H", [
+    (8, 256, 64, 64, 1, 2),      # the tiny workload's shape
+    (5, 300, 128, 128, 2, 2),    # ragged: last tile 92 rows
+    (7, 100, 64, 64, 1, 2),      # ragged: last tile 60 rows
+    (3, 40, 128, 128, 1, 1),     # one partial tile
+    (66, 256, 128, 128, 1, 1),   # the training workload's frame count at s = 256
+])
+def test_backward_small(f, s, T, D, B, H):
+    N = f * s
+    scale = 1.0 / np.sqrt(D)
+    _say(f"[bwd] f={f} s={s} T={T} D={D} B={B} H={H}")
+    q, k, v, do = workloads.make_inputs(B, H, N, D, 100 + f, with_dout=True)
+    L = sba.Layout(f, s, T)
+    qc, kc, vc, dc = q.cuda(), k.cuda(), v.cuda(), do.cuda()
+    o, lse = sba.attn_fwd(qc, kc, vc, L, scale)
+    dq, dk, dv = sba.attn_bwd(qc, kc, vc, o, lse, dc, L, scale)
+    torch.cuda.synchronize()
+    kept = om.kept_tiles(f, s, T, True)
+    for b in range(B):
+        for h in range(H):
+            rq, rk, rv = oa.bwd(f64(q[b, h]), f64(k[b, h]), f64(v[b, h]), f64(do[b, h]), kept, T,
+                                scale)
+            check_close(f64(dq[b, h]), rq, f"dQ b={b} h={h}", normalise=True)
+            check_close(f64(dk[b, h]), rk, f"dK b={b} h={h}", normalise=True)
+            check_close(f64(dv[b, h]), rv, f"dV b={b} h={h}", normalise=True)
+
+
+def test_backward_sink_off_and_peaky():
+    f, s, T, D = 9, 200, 128, 128
+    N = f * s
+    scale = 8.0 / np.sqrt(D)
+    q, k, v, do = workloads.make_inputs(1, 1, N, D, 201, with_dout=True)
+    L = sba.Layout(f, s, T, sink=False)
+    qc, kc, vc, dc = q.cuda(), k.cuda(), v.cuda(), do.cuda()
+    o, lse = sba.attn_fwd(qc, kc, vc, L, scale)
+    dq, dk, dv = sba.attn_bwd(qc, kc, vc, o, lse, dc, L, scale)
+    kept = om.kept_tiles(f, s, T, False)
+    rq, rk, rv = oa.bwd(f64(q[0, 0]), f64(k[0, 0]), f64(v[0, 0]), f64(do[0, 0]), kept, T, scale)
+    check_close(f64(dq[0, 0]), rq, "dQ", normalise=True)
+    check_close(f64(dk[0, 0]), rk, "dK", normalise=True)
+    check_close(f64(dv[0, 0]), rv, "dV", normalise=True)
+
+
+def test_backward_deterministic():
+    f, s, T, D = 6, 300, 128, 128
+    q, k, v, do = (t.cuda() for t in workloads.make_inputs(1, 2, f * s, D, 301, with_dout=True))
+    L = sba.Layout(f, s, T)
+    o, lse = sba.attn_fwd(q, k, v, L)
+    a = sba.attn_bwd(q, k, v, o, lse, do, L)
+    b = sba.attn_bwd(q, k, v, o, lse, do, L)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def test_full_size_training_step():
+    w = workloads.WORKLOADS["train_f66"]
+    _say(f"[bwd-full] {w.name} B={w.B} H={w.H} N={w.N} D={w.D}")
+    q, k, v, do = workloads.workload_inputs(w, device="cuda")
+    L = sba.Layout(w.frames, w.tokens_per_frame, w.T)
+    o, lse = sba.attn_fwd(q, k, v, L, w.scale)
+    dq, dk, dv = sba.attn_bwd(q, k, v, o, lse, do, L, w.scale)
+    torch.cuda.synchronize()
+    for t in (dq, dk, dv):
+        assert bool(torch.isfinite(t.float()).all())
+    # identities over every head
+    sdv = dv.double().sum(dim=2)
+    sdo = do.double().sum(dim=2)
+    rms_dv = float(dv.double().pow(2).mean().sqrt())
+    # each of N bf16-rounded terms is off by <= 2^-9 relative: the sum's
+    # error grows like sqrt(N) * 2^-9 * rms
+    tol = 8 * np.sqrt(w.N) * 2.0 ** -9 * max(rms_dv, float(do.double().pow(2).mean().sqrt()))
+    assert float((sdv - sdo).abs().max()) <= tol, (float((sdv - sdo).abs().max()), tol)
+    sdk = dk.double().sum(dim=2)
+    rms_dk = float(dk.double().pow(2).mean().sqrt())
+    assert float(sdk.abs().max()) <= 8 * np.sqrt(w.N) * 2.0 ** -9 * rms_dk + 1e-6
+    # dQ on sampled query tiles of the first and last heads
+    kept = om.kept_tiles(w.frames, w.tokens_per_frame, w.T, True)
+    for h in (0, w.H - 1):
+        qh, kh, vh, dh = f64(q[0, h]), f64(k[0, h]), f64(v[0, h]), f64(do[0, h])
+        for u in sample_tiles(w.N, w.T, w.tokens_per_frame, seed=5)[:4]:
+            rows = slice(u * w.T, min(w.N, (u + 1) * w.T))
+            rq = oa.bwd_dq_tile(qh, kh, vh, dh, kept, w.T, w.scale, u)
+            check_close(f64(dq[0, h, rows]), rq, f"dQ h={h} tile={u}", normalise=True)

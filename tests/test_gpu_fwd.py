@@ -1,0 +1,166 @@
+"""GPU parity of the forward pass against the oracle (needs an MI355X).
+
+Every call goes through the C ABI (static_block_sparse_amd -> libradial.so).
+Small shapes are compared element by element over every head and row; the
+full-size workloads in the launch configuration bench.py times are compared
+on sampled query tiles, plus properties that hold at any size.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import static_block_sparse_amd as sba
+import workloads
+from gpu_util import check_close, check_lse, f64, sample_tiles
+from oracle import attention as oa
+from oracle import mask as om
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def _run_full_compare(f, s, T, D, B, H, seed, sink=True, scale=None, dense=False, v_ones=False):
+    N = f * s
+    scale = 1.0 / np.sqrt(D) if scale is None else scale
+    _say(f"[fwd] f={f} s={s} T={T} D={D} B={B} H={H} seed={seed} sink={sink} dense={dense}")
+    q, k, v = workloads.make_inputs(B, H, N, D, seed)
+    if v_ones:
+        v = torch.ones_like(v)
+    L = sba.Layout(f, s, T, sink=sink, dense=dense)
+    o, lse = sba.attn_fwd(q.cuda(), k.cuda(), v.cuda(), L, scale)
+    torch.cuda.synchronize()
+    kept = np.ones((L.n_blocks,) * 2, bool) if dense else om.kept_tiles(f, s, T, sink)
+    go, gl = f64(o), f64(lse)
+    stats = []
+    for b in range(B):
+        for h in range(H):
+            ro, rl = oa.fwd(f64(q[b, h]), f64(k[b, h]), f64(v[b, h]), kept, T, scale)
+            stats.append(check_close(go[b, h], ro, f"O b={b} h={h}"))
+            check_lse(gl[b, h], rl)
+    return go, stats
+
+
+def test_tiny_workload_all_heads():
+    w = workloads.WORKLOADS["tiny_f8_s256"]
+    _run_full_compare(w.frames, w.tokens_per_frame, w.T, w.D, w.B, w.H, w.seed)
+
+
+@pytest.mark.parametrize("f,s,T,D,B,H", [
+    (5, 300, 128, 128, 2, 3),    # N = 1500: 12 tiles, last one 92 rows; tiles straddle frames
+    (7, 100, 64, 64, 1, 2),      # N = 700: last tile 60 rows; 64-tiles span frames
+    (3, 40, 128, 128, 1, 1),     # a single, partial tile (N = 120 < T)
+    (40, 20, 64, 64, 1, 1),      # many frames, narrow bands, rows of very different length
+    (300, 2, 64, 64, 1, 1),      # tiny frames: the width-below-one sampling fires
+])
+def test_ragged_shapes(f, s, T, D, B, H):
+    _run_full_compare(f, s, T, D, B, H, seed=11 + f)
+
+
+def test_sink_off():
+    _run_full_compare(9, 200, 128, 128, 1, 2, seed=21, sink=False)
+
+
+def test_v_ones_gives_ones():
+    # every softmax row sums to one, so V == 1 must give O == 1
+    f, s, T, D = 9, 200, 128, 128
+    N = f * s
+    q, k, _ = workloads.make_inputs(1, 2, N, D, 31)
+    v = torch.ones((1, 2, N, D), dtype=torch.bfloat16)
+    o, _ = sba.attn_fwd(q.cuda(), k.cuda(), v.cuda(), sba.Layout(f, s, T))
+    err = float((o.double() - 1).abs().max())
+    assert err <= 4e-3, err
+
+
+def test_peaky_softmax():
+    # scale x8: logits with std ~8, so a few keys dominate each row
+    _run_full_compare(6, 300, 128, 128, 1, 2, seed=41, scale=8.0 / np.sqrt(128))
+    _run_full_compare(8, 256, 64, 64, 1, 2, seed=42, scale=8.0 / np.sqrt(64))
+
+
+def test_dense_layout_is_plain_attention():
+    go, _ = _run_full_compare(4, 300, 128, 128, 1, 2, seed=51, dense=True)
+    # and against torch's float64 SDPA on the CPU (a library routine)
+    q, k, v = workloads.make_inputs(1, 2, 1200, 128, 51)
+    ref = torch.nn.functional.scaled_dot_product_attention(q.double(), k.double(), v.double())
+    assert float(np.abs(go - ref.numpy()).max()) <= 2e-2
+
+
+def test_two_frames_equal_dense_layout_bitwise():
+    # f = 2 keeps every tile, so the radial and the dense layouts run the
+    # same tiles in the same order
+    f, s, T, D = 2, 700, 128, 128
+    q, k, v = (t.cuda() for t in workloads.make_inputs(1, 2, f * s, D, 61))
+    a, la = sba.attn_fwd(q, k, v, sba.Layout(f, s, T))
+    b, lb = sba.attn_fwd(q, k, v, sba.Layout(f, s, T, dense=True))
+    assert torch.equal(a, b) and torch.equal(la, lb)
+
+
+def test_deterministic_and_stream_aware():
+    f, s, T, D = 6, 300, 128, 128
+    q, k, v = (t.cuda() for t in workloads.make_inputs(2, 3, f * s, D, 71))
+    L = sba.Layout(f, s, T)
+    a, la = sba.attn_fwd(q, k, v, L)
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        b, lb = sba.attn_fwd(q, k, v, L)
+    torch.cuda.current_stream().wait_stream(st)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b) and torch.equal(la, lb)
+
+
+def test_rejects_bad_inputs_on_gpu():
+    L = sba.Layout(8, 256, 64)
+    q = torch.zeros((1, 1, 2048, 64), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(sba.RadialError):
+        sba.attn_fwd(q, q, q, sba.Layout(8, 255, 64))
+    with pytest.raises(sba.RadialError):
+        sba.attn_fwd(q, q, q, sba.Layout(8, 256, 128))
+    # misaligned pointer: a view offset by one element
+    raw = torch.zeros(2048 * 64 + 8, dtype=torch.bfloat16, device="cuda")
+    lib = sba.lib()
+    L.upload()
+    o = torch.empty_like(q)
+    lse = torch.empty((1, 1, 2048), dtype=torch.float32, device="cuda")
+    st = lib.radial_attn_fwd(L.handle, 1, 1, 2048, 64, 0.125, raw.data_ptr() + 2, q.data_ptr(),
+                             q.data_ptr(), o.data_ptr(), lse.data_ptr(), None)
+    assert st == -1
+
+
+FULL = ["hunyuan_5s_720p", "wan21_720p", "hunyuan_4x_long", "train_f66"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_sampled_tiles(name):
+    """Full-size workload, all heads in one launch (as bench.py times it);
+    oracle check on sampled query tiles of the first and last heads; every
+    output finite."""
+    w = workloads.WORKLOADS[name]
+    _say(f"[fwd-full] {name} B={w.B} H={w.H} N={w.N} D={w.D}")
+    q, k, v = workloads.workload_inputs(w, with_dout=False, device="cuda")
+    L = sba.Layout(w.frames, w.tokens_per_frame, w.T)
+    o, lse = sba.attn_fwd(q, k, v, L, w.scale)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(lse).all())
+    assert bool(torch.isfinite(o.float()).all())
+    kept = om.kept_tiles(w.frames, w.tokens_per_frame, w.T, True)
+    tiles = sample_tiles(w.N, w.T, w.tokens_per_frame, seed=w.seed)
+    for h in (0, w.H - 1):
+        qh, kh, vh = f64(q[0, h]), f64(k[0, h]), f64(v[0, h])
+        for u in tiles:
+            rows = slice(u * w.T, min(w.N, (u + 1) * w.T))
+            ro, rl = oa.fwd_tile(qh, kh, vh, kept, w.T, w.scale, u)
+            check_close(f64(o[0, h, rows]), ro, f"{name} O h={h} tile={u}")
+            check_lse(f64(lse[0, h, rows]), rl, f"{name} lse h={h} tile={u}")

@@ -141,3 +141,15 @@ def test_backward_finite_differences():
                 args[which][idx] -= 2 * h
                 dn = loss(*args)
                 assert abs((up - dn) / (2 * h) - grad[idx]) < 1e-7
+
+
+def test_dq_tile_matches_full_backward():
+    f, s, T, d = 6, 11, 8, 4
+    n = f * s
+    q, k, v, do = (_rand((n, d), 60 + i) for i in range(4))
+    kept = om.kept_tiles(f, s, T, True)
+    dq, _, _ = oa.bwd(q, k, v, do, kept, T, 0.7)
+    for u in range(kept.shape[0]):
+        rows = slice(u * T, min(n, (u + 1) * T))
+        np.testing.assert_allclose(oa.bwd_dq_tile(q, k, v, do, kept, T, 0.7, u), dq[rows],
+                                   rtol=0, atol=1e-12)

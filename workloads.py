@@ -60,31 +60,34 @@ WORKLOADS = {
 ORDER = ["tiny_f8_s256", "hunyuan_5s_720p", "wan21_720p", "hunyuan_4x_long", "train_f66"]
 
 
-def randn_bf16(shape, gen: torch.Generator) -> torch.Tensor:
-    """i.i.d. N(0,1) drawn in float32 on the CPU, rounded to bf16 (RNE)."""
-    return torch.randn(shape, generator=gen, dtype=torch.float32).to(torch.bfloat16)
+def randn_bf16(shape, gen: torch.Generator, device="cpu") -> torch.Tensor:
+    """i.i.d. N(0,1) drawn in float32, rounded to bf16 (round to nearest even)."""
+    return torch.randn(shape, generator=gen, dtype=torch.float32, device=device).to(torch.bfloat16)
 
 
 def make_inputs(B: int, H: int, N: int, D: int, seed: int, with_dout: bool = False,
-                heads=None):
-    """Q, K, V (and dO) as CPU bf16 tensors [B, H, N, D], drawn in that order
-    from ``torch.Generator('cpu').manual_seed(seed)``.
+                heads=None, device="cpu"):
+    """Q, K, V (and dO) as bf16 tensors [B, H, N, D], drawn in that order from
+    a ``torch.Generator(device).manual_seed(seed)``.
 
+    ``device="cpu"`` (default) draws with torch's CPU generator; a GPU device
+    draws with torch's GPU generator directly in device memory (fast for the
+    full-size shapes; a different but equally seeded stream of values).
     ``heads``: optionally keep only these head indices of the full draw (the
     draw itself is always the full [B, H, N, D] so values do not depend on
     which heads are kept).
     """
-    g = torch.Generator("cpu").manual_seed(seed)
+    g = torch.Generator(device).manual_seed(seed)
     names = ["q", "k", "v"] + (["do"] if with_dout else [])
     out = []
     for _ in names:
-        t = randn_bf16((B, H, N, D), g)
+        t = randn_bf16((B, H, N, D), g, device)
         if heads is not None:
             t = t[:, list(heads)].contiguous()
         out.append(t)
     return tuple(out)
 
 
-def workload_inputs(w: Workload, with_dout: bool | None = None, heads=None):
+def workload_inputs(w: Workload, with_dout: bool | None = None, heads=None, device="cpu"):
     wd = w.backward if with_dout is None else with_dout
-    return make_inputs(w.B, w.H, w.N, w.D, w.seed, wd, heads)
+    return make_inputs(w.B, w.H, w.N, w.D, w.seed, wd, heads, device)
