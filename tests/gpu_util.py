@@ -19,6 +19,14 @@ Tolerances (forward, bf16 inputs, fp32 accumulation):
   and dS, the same error structure as O, so the same relative guards apply
   against rms of the reference gradient, together with the absolute bounds
   on values normalised by max(1, rms(ref)).
+* Peaky softmax gradients (logit std ~8): the backward receives O rounded to
+  bf16, so Delta = rowsum(dO * O) is off by up to
+  eps ~ 2^-9 * sum_d |dO| |O| ~ 2^-9 * sqrt(D) ~ 0.02 per row (3 sigma ~0.06)
+  when O is close to a single V row.  That shifts every dS entry of the row
+  by P * eps and dQ by scale * eps * (P-weighted mean of K rows), up to
+  scale * 0.06 * 3 ~ 0.13 at scale 8/sqrt(128): about 5.5% of rms(dQ) ~ 2.4.
+  Diffuse softmax rows average this away; peaky ones do not.  Peaky
+  gradients therefore use max |dG| <= PEAKY_REL_MAX * rms(G_ref).
 """
 
 from __future__ import annotations
@@ -31,6 +39,7 @@ O_MEAN_ABS = 2e-3
 REL_MAX = 5e-2
 REL_MEAN = 1e-2
 LSE_MAX_ABS = 1e-3
+PEAKY_REL_MAX = 1e-1
 
 
 def f64(t: torch.Tensor) -> np.ndarray:
@@ -38,7 +47,7 @@ def f64(t: torch.Tensor) -> np.ndarray:
 
 
 def check_close(got: np.ndarray, ref: np.ndarray, what: str, absolute: bool = True,
-                normalise: bool = False):
+                normalise: bool = False, rel_max: float = REL_MAX, rel_mean: float = REL_MEAN):
     """Assert the forward/gradient tolerances above; returns the error stats."""
     assert got.shape == ref.shape, (what, got.shape, ref.shape)
     assert np.isfinite(got).all(), f"{what}: non-finite values"
@@ -50,8 +59,8 @@ def check_close(got: np.ndarray, ref: np.ndarray, what: str, absolute: bool = Tr
         assert stats["max_abs"] / norm <= O_MAX_ABS, (what, stats)
         assert stats["mean_abs"] / norm <= O_MEAN_ABS, (what, stats)
     if rms > 0:
-        assert stats["max_abs"] <= REL_MAX * rms, (what, stats)
-        assert stats["mean_abs"] <= REL_MEAN * rms, (what, stats)
+        assert stats["max_abs"] <= rel_max * rms, (what, stats)
+        assert stats["mean_abs"] <= rel_mean * rms, (what, stats)
     return stats
 
 

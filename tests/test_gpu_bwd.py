@@ -15,7 +15,7 @@ import torch
 
 import static_block_sparse_amd as sba
 import workloads
-from gpu_util import check_close, f64, sample_tiles
+from gpu_util import PEAKY_REL_MAX, check_close, f64, sample_tiles
 from oracle import attention as oa
 from oracle import mask as om
 
@@ -70,9 +70,9 @@ def test_backward_sink_off_and_peaky():
     dq, dk, dv = sba.attn_bwd(qc, kc, vc, o, lse, dc, L, scale)
     kept = om.kept_tiles(f, s, T, False)
     rq, rk, rv = oa.bwd(f64(q[0, 0]), f64(k[0, 0]), f64(v[0, 0]), f64(do[0, 0]), kept, T, scale)
-    check_close(f64(dq[0, 0]), rq, "dQ", normalise=True)
-    check_close(f64(dk[0, 0]), rk, "dK", normalise=True)
-    check_close(f64(dv[0, 0]), rv, "dV", normalise=True)
+    # Delta from the bf16 O dominates here (see gpu_util): relative bound only
+    for got, ref, name in ((dq, rq, "dQ"), (dk, rk, "dK"), (dv, rv, "dV")):
+        check_close(f64(got[0, 0]), ref, name, absolute=False, rel_max=PEAKY_REL_MAX)
 
 
 def test_backward_deterministic():
