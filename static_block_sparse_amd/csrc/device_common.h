@@ -76,6 +76,54 @@ __device__ __forceinline__ void st4(bf16 *p, bf16x4 v) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Swizzled element offset of 16-byte block `ch` of row `row` in a row-major
+// [rows][D] bf16 LDS tile (no padding).  The block index is XORed with
+// f(row) = 2 * (row % H) + (row / H) % 2 (mod D/8, H = D/16): 16 consecutive
+// rows reading the same block, and the 4 rows x 2 blocks of a transposing
+// read, land in distinct bank groups.
+template <int D>
+__device__ __forceinline__ int swz(int row, int ch) {
+  constexpr int NCH = D / 8, H = NCH / 2;
+  const int f = (2 * (row % H) + (row / H) % 2) % NCH;
+  return row * D + 8 * (ch ^ f);
+}
+
+// max / sum of x over the lane pair (l, l ^ 32) (gfx950 v_permlane32_swap)
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+// Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
+// lane i supplies the address of 4 consecutive bf16 of row r0 + i / 4 at
+// columns c0 + 4 (i % 4) (a 4 x 16 block); lane i receives column c0 + i of
+// rows r0 .. r0 + 3.
+__device__ __forceinline__ bf16x4 ld_tr(const bf16 *p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(p));
+}
+
+// Raw buffer resource over `bytes` bytes at p (gfx9 data-format word).
+// Loads at offsets >= bytes return zeros, which is how rows past the end of
+// a sequence are padded without branches.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, bytes, 0x00020000);
+}
+
+__device__ __forceinline__ bf16x8 buf_ld8(__amdgpu_buffer_rsrc_t r, int byte_off) {
+  typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0);
+  return __builtin_bit_cast(bf16x8, v);
+}
+
 // Work-item remap so that each XCD (of 8) processes one contiguous range
 // of work items: the hardware hands consecutive workgroups to XCDs round
 // robin, so workgroup b runs on XCD b % 8.  Bijective on [0, n).
