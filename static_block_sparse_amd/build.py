@@ -39,31 +39,33 @@ def _run(cmd):
     return out
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link libradial.so; returns its path."""
+def build(verbose: bool = False, defines=(), out: str = LIB) -> str:
+    """Compile every source and link libradial.so (or `out`); returns its path.
+    `defines`: extra NAME=VALUE preprocessor definitions (tuning constants)."""
     if not os.path.exists(HIPCC):
         raise RuntimeError(f"hipcc not found at {HIPCC}")
     tmp = tempfile.mkdtemp(prefix="radial_build_")
     try:
         objs = []
+        dflags = [f"-D{d}" for d in defines]
         for src in SOURCES:
             obj = os.path.join(tmp, src + ".o")
             path = os.path.join(CSRC, src)
             if src.endswith(".hip"):
-                cmd = [HIPCC, "-x", "hip", *DEVICE, *COMMON, "-c", path, "-o", obj]
+                cmd = [HIPCC, "-x", "hip", *DEVICE, *COMMON, *dflags, "-c", path, "-o", obj]
             else:
                 cmd = [HIPCC, *COMMON, "-D__HIP_PLATFORM_AMD__", "-c", path, "-o", obj]
-            out = _run(cmd)
-            if verbose and out.strip():
-                print(out)
+            msg = _run(cmd)
+            if verbose and msg.strip():
+                print(msg)
             objs.append(obj)
         tmp_lib = os.path.join(tmp, "libradial.so")
         _run([HIPCC, *DEVICE, "-shared", "-fPIC", "-o", tmp_lib, *objs])
-        shutil.copyfile(tmp_lib, LIB + ".tmp")
-        os.replace(LIB + ".tmp", LIB)
+        shutil.copyfile(tmp_lib, out + ".tmp")
+        os.replace(out + ".tmp", out)
     finally:
         shutil.rmtree(tmp, ignore_errors=True)
-    return LIB
+    return out
 
 
 if __name__ == "__main__":

@@ -83,7 +83,7 @@ __global__ __launch_bounds__(T / 32 * 64, 1) void radial_bwd_dkdv_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int c32 = lane & 31, g = lane >> 5;
-  const int work = xcd_remap(blockIdx.x, n_work);
+  const int work = xcd_remap(blockIdx.x, n_work, 0);
   const int bh = work / nb;
   const int v = col_order[work - bh * nb];
   const int64_t base = (int64_t)bh * N * D;
@@ -214,7 +214,7 @@ __global__ __launch_bounds__(T / 32 * 64, 2) void radial_bwd_dq_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int c32 = lane & 31, g = lane >> 5;
-  const int work = xcd_remap(blockIdx.x, n_work);
+  const int work = xcd_remap(blockIdx.x, n_work, 0);
   const int bh = work / nb;
   const int u = work - bh * nb;
   const int64_t base = (int64_t)bh * N * D;

@@ -17,12 +17,14 @@
 //    one query per lane column: a row's max and sum need one exchange
 //    between lanes l and l ^ 32 (v_permlane32_swap), and P feeds P V as the
 //    B operand with no lane movement (see device_common.h).
-//  * K and V chunks are staged row-major in LDS with an XOR swizzle of the
-//    16-byte column blocks; the V^T operand is read with the gfx950
-//    transposing LDS load (ds_read_b64_tr_b16).
-//  * chunks are double buffered: the next chunk's global loads are issued
-//    into registers at the start of a chunk and written to the other LDS
-//    buffer after its products, so there is one barrier per chunk.
+//  * K and V chunks sit row-major in LDS with an XOR swizzle of the 16-byte
+//    column blocks; the V^T operand is read with the gfx950 transposing LDS
+//    load (ds_read_b64_tr_b16).
+//  * K and V chunks are copied global -> LDS by the buffer unit directly (no
+//    staging registers); the swizzle is chosen through each lane's source
+//    offset and keys past N read as zeros.  Chunks are double buffered: the
+//    copy of chunk c + 1 is issued before the products of chunk c, with one
+//    barrier per chunk.
 //  * the running max is only moved when a chunk's max exceeds it by more
 //    than 8 (log2 units); probabilities then stay below 2^8, exact in the
 //    final O / l and LSE, and the O rescale is skipped on most chunks.
@@ -30,6 +32,10 @@
 
 #include "device_common.h"
 #include "kernels.h"
+
+#ifndef RADIAL_FWD_XCD_BLOCK
+#define RADIAL_FWD_XCD_BLOCK 16  // query tiles per XCD block (see xcd_remap)
+#endif
 
 namespace radial {
 
@@ -42,10 +48,10 @@ struct FwdCfg {
   static constexpr int NKB = KC / 32;   // 32-key blocks per chunk
   static constexpr int NDB = D / 32;    // 32-wide blocks of the head dim
   static constexpr int NKK = D / 16;    // K steps of the Q K^T product
-  static constexpr int NCH = D / 8;     // 16-byte blocks per row
-  static constexpr int LPT = KC * NCH / NT;  // 16-byte loads per thread per operand
-  static constexpr int BUF = 2 * KC * D;     // elements per buffer (K then V)
-  static_assert(LPT >= 1 && KC * NCH % NT == 0, "chunk must split evenly");
+  static constexpr int CHUNK = KC * D;  // elements of one staged operand
+  static constexpr int BUF = 2 * CHUNK; // elements per buffer (K then V)
+  static constexpr int NDMA = CHUNK * 2 / 1024 / NW;  // 1 KB copies per wave per operand
+  static_assert(NDMA >= 1 && CHUNK * 2 % (1024 * NW) == 0, "chunk must split evenly");
 };
 
 template <int D, int T>
@@ -56,12 +62,12 @@ __global__ __launch_bounds__(T / 32 * 64, 2) void radial_fwd_kernel(
     float scale_log2) {
   using C = FwdCfg<D, T>;
   constexpr float kSlack = 8.f;  // lazy-rescale threshold (log2 units)
-  __shared__ __attribute__((aligned(16))) bf16 lds[2 * C::BUF];
+  __shared__ __attribute__((aligned(1024))) bf16 lds[2 * C::BUF];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int c32 = lane & 31, g = lane >> 5;
-  const int work = xcd_remap(blockIdx.x, n_work);
+  const int work = xcd_remap(blockIdx.x, n_work, RADIAL_FWD_XCD_BLOCK);
   const int bh = work / nb;
   const int u = work - bh * nb;
   const int64_t base = (int64_t)bh * N * D;
@@ -87,28 +93,28 @@ __global__ __launch_bounds__(T / 32 * 64, 2) void radial_fwd_kernel(
     return col_idx[t_begin + c / C::CPT] * T + (c % C::CPT) * C::KC;
   };
 
-  // chunk staging: thread `tid` moves the 16-byte blocks idx = tid + it * NT
-  // (row idx / NCH, block idx % NCH); buffer loads past N read zeros
-  bf16x8 pk[C::LPT], pv[C::LPT];
-  auto load_chunk = [&](int k0) {
+  // Chunk staging by direct global -> LDS copies (no staging registers):
+  // copy jj of this wave fills LDS bytes [(wave*NDMA + jj) * 1024, +1024) of
+  // an operand; lane l writes element e = blk*512 + 8l, i.e. row e / D and
+  // physical 16-byte block (e % D) / 8, which holds logical block
+  // physical ^ swz_f(row) of that row.  Lanes past N write zeros.
+  int dma_off[C::NDMA];
+#pragma unroll
+  for (int jj = 0; jj < C::NDMA; ++jj) {
+    const int e = (wave * C::NDMA + jj) * 512 + 8 * lane;
+    const int row = e / D, pblk = (e % D) / 8;
+    dma_off[jj] = row * D * 2 + 16 * (pblk ^ swz_f<D>(row));
+  }
+  auto issue_copy = [&](int buf, int k0) {
     const int bytes = (N - k0) * D * 2;
     const auto rk = make_rsrc(Kb + (int64_t)k0 * D, bytes);
     const auto rv = make_rsrc(Vb + (int64_t)k0 * D, bytes);
-#pragma unroll
-    for (int it = 0; it < C::LPT; ++it) {
-      pk[it] = buf_ld8(rk, (tid + it * C::NT) * 16);
-      pv[it] = buf_ld8(rv, (tid + it * C::NT) * 16);
-    }
-  };
-  auto store_chunk = [&](int buf) {
     bf16 *kd = lds + buf * C::BUF;
-    bf16 *vd = kd + C::KC * D;
 #pragma unroll
-    for (int it = 0; it < C::LPT; ++it) {
-      const int idx = tid + it * C::NT;
-      const int row = idx / C::NCH, ch = idx % C::NCH;
-      st8(kd + swz<D>(row, ch), pk[it]);
-      st8(vd + swz<D>(row, ch), pv[it]);
+    for (int jj = 0; jj < C::NDMA; ++jj) {
+      const int blk = (wave * C::NDMA + jj) * 512;
+      dma16(rk, kd + blk, dma_off[jj]);
+      dma16(rv, kd + C::CHUNK + blk, dma_off[jj]);
     }
   };
 
@@ -120,13 +126,8 @@ __global__ __launch_bounds__(T / 32 * 64, 2) void radial_fwd_kernel(
 
   int key_next = nchunks > 0 ? chunk_key0(0) : 0;            // chunk c + 1
   int key_after = nchunks > 1 ? chunk_key0(1) : 0;           // chunk c + 2
-  if (nchunks > 0) {
-    load_chunk(key_next);
-    store_chunk(0);
-  }
-  // Q fragments have landed on every path into the loop, so no wait for
-  // them is left inside it (vmcnt(0); expcnt and lgkmcnt at their maximum)
-  __builtin_amdgcn_s_waitcnt(0x0F70);
+  if (nchunks > 0) issue_copy(0, key_next);
+  wait_vmem();  // Q fragments and the first chunk
   __syncthreads();
 
   // lane (g, c32) in transposing-read group G = lane / 16 addresses row
@@ -138,22 +139,32 @@ __global__ __launch_bounds__(T / 32 * 64, 2) void radial_fwd_kernel(
     const bf16 *Vs = Ks + C::KC * D;
     const int key0 = key_next;
     key_next = key_after;
-    // next chunk's global loads fly during this chunk's products
-    if (c + 1 < nchunks) load_chunk(key_next);
+    // the next chunk's copy lands in the other buffer during these products
+    if (c + 1 < nchunks) issue_copy((c + 1) & 1, key_next);
     if (c + 2 < nchunks) key_after = chunk_key0(c + 2);
 
-    // S^T for the wave's 32 queries against the chunk's KC keys
+    // S^T for the wave's 32 queries against the chunk's KC keys.  The K
+    // fragments of block kb + 1 are read while block kb's products run, so
+    // the LDS latency is paid once per chunk rather than once per product.
     f32x16 s[C::NKB];
+    bf16x8 kf[C::NKB][C::NKK];
+#pragma unroll
+    for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+      for (int kk = 0; kk < C::NKK; ++kk) kf[kb][kk] = ld8(Ks + swz<D>(kb * 32 + c32, 2 * kk + g));
 #pragma unroll
     for (int kb = 0; kb < C::NKB; ++kb) {
-      const int row = kb * 32 + c32;
-      bf16x8 kf[C::NKK];
-#pragma unroll
-      for (int kk = 0; kk < C::NKK; ++kk) kf[kk] = ld8(Ks + swz<D>(row, 2 * kk + g));
       s[kb] = zero16();
 #pragma unroll
-      for (int kk = 0; kk < C::NKK; ++kk) s[kb] = mfma32(kf[kk], qf[kk], s[kb]);
+      for (int kk = 0; kk < C::NKK; ++kk) s[kb] = mfma32(kf[kb][kk], qf[kk], s[kb]);
     }
+    __builtin_amdgcn_sched_group_barrier(0x100, C::NKK, 1);  // block 0 reads
+#pragma unroll
+    for (int i = 0; i < C::NKK * (C::NKB - 1); ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);     // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);     // next block's read
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, C::NKK, 1);  // last block's MFMAs
     if (key0 + C::KC > N) {  // the tail chunk: keys at or past N get -inf
       // register r of block kb holds key key0 + kb*32 + 8*(r/4) + 4g + r%4
       const int lim = N - key0 - 4 * g;
@@ -181,15 +192,17 @@ __global__ __launch_bounds__(T / 32 * 64, 2) void radial_fwd_kernel(
     }
 
     bf16x8 pf[C::NKB][2];
+    float psum[4] = {0.f, 0.f, 0.f, 0.f};  // four partial sums: short add chains
 #pragma unroll
     for (int kb = 0; kb < C::NKB; ++kb) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float p = fast_exp2(fmaf(s[kb][r], scale_log2, -m_run));
-        l_run += p;
+        psum[r & 3] += p;
         pf[kb][r >> 3][r & 7] = bf16(p);
       }
     }
+    l_run += (psum[0] + psum[1]) + (psum[2] + psum[3]);
 
     // O^T += V^T P^T
 #pragma unroll
@@ -206,9 +219,18 @@ __global__ __launch_bounds__(T / 32 * 64, 2) void radial_fwd_kernel(
         }
       }
     }
+    // transposing reads run four ahead of the products that consume them
+    constexpr int NPV = C::NDB * C::NKB * 2;
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 2);
+#pragma unroll
+    for (int i = 0; i < NPV - 2; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 2);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 2);
 
-    if (c + 1 < nchunks) store_chunk((c + 1) & 1);
-    __syncthreads();
+    wait_vmem();      // this wave's copies of chunk c + 1 have landed
+    __syncthreads();  // ... everyone's, and chunk c is no longer read
   }
 
   const float l_tot = pair_sum(l_run);

@@ -82,10 +82,14 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // rows reading the same block, and the 4 rows x 2 blocks of a transposing
 // read, land in distinct bank groups.
 template <int D>
-__device__ __forceinline__ int swz(int row, int ch) {
+__device__ __forceinline__ int swz_f(int row) {
   constexpr int NCH = D / 8, H = NCH / 2;
-  const int f = (2 * (row % H) + (row / H) % 2) % NCH;
-  return row * D + 8 * (ch ^ f);
+  return (2 * (row % H) + (row / H) % 2) % NCH;
+}
+
+template <int D>
+__device__ __forceinline__ int swz(int row, int ch) {
+  return row * D + 8 * (ch ^ swz_f<D>(row));
 }
 
 // max / sum of x over the lane pair (l, l ^ 32) (gfx950 v_permlane32_swap)
@@ -124,14 +128,40 @@ __device__ __forceinline__ bf16x8 buf_ld8(__amdgpu_buffer_rsrc_t r, int byte_off
   return __builtin_bit_cast(bf16x8, v);
 }
 
-// Work-item remap so that each XCD (of 8) processes one contiguous range
-// of work items: the hardware hands consecutive workgroups to XCDs round
-// robin, so workgroup b runs on XCD b % 8.  Bijective on [0, n).
-__device__ __forceinline__ int xcd_remap(int b, int n) {
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Direct global-to-LDS copy (gfx950 buffer_load_dwordx4 ... lds): lane l
+// copies the 16 bytes at `byte_off` of the buffer to LDS address
+// lds_block + 16 * l; lanes past the end of the buffer write zeros.  The
+// data is visible to other waves after s_waitcnt vmcnt(0) and a barrier.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, bf16 *lds_block, int byte_off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)lds_block, 16, byte_off, 0, 0, 0);
+}
+
+// s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maximum)
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Work-item order for a launch of n workgroups whose work items are
+// numbered head-major (query tile fastest).  The hardware hands workgroups to
+// the 8 XCDs round robin (workgroup b runs on XCD b % 8).  Work is dealt to
+// the XCDs in blocks of `blk` consecutive items: XCD x takes blocks
+// x, x + 8, x + 16, ... in order.  At any moment the XCDs then work on 8
+// neighbouring blocks of the same head, so the key/value tiles in use across
+// the chip are those of about one head (they stay in the memory-side cache)
+// and the workgroups sharing one XCD's L2 work on neighbouring query tiles.
+// Items past the last full round of 8 blocks keep their own index.
+// Bijective on [0, n).  blk == 0: XCD x takes one contiguous range.
+__device__ __forceinline__ int xcd_remap(int b, int n, int blk) {
   constexpr int X = 8;
-  const int q = n / X, r = n % X;
+  if (blk == 0) {
+    const int q = n / X, r = n % X;
+    const int x = b % X, k = b / X;
+    return (x < r) ? x * (q + 1) + k : r * (q + 1) + (x - r) * q + k;
+  }
+  const int main_part = n / (X * blk) * (X * blk);
+  if (b >= main_part) return b;
   const int x = b % X, k = b / X;
-  return (x < r) ? x * (q + 1) + k : r * (q + 1) + (x - r) * q + k;
+  return ((k / blk) * X + x) * blk + k % blk;
 }
 
 // Rows [0, ROWS) x cols [0, D) of a row-major bf16 tile into LDS with row
