@@ -117,7 +117,7 @@ def cpu_baseline(w, layout_kept, budget_s: float = 15.0):
     sizes = np.full(nb, w.T)
     sizes[-1] = w.N - (nb - 1) * w.T
     t_start = time.perf_counter()
-    order = list(range(0, nb, max(1, nb // 64)))
+    order = list(range(0, nb, max(1, nb // 512)))
     done, pairs = 0, 0
     for u in order:
         oa.fwd_tile(qh, kh, vh, layout_kept, w.T, w.scale, u)
