@@ -13,10 +13,18 @@
 //   2. dkdv: one workgroup per key tile, walking its CSC column of query
 //            tiles; dK and dV stay in registers for the whole walk
 //   3. dq:   one workgroup per query tile, walking its CSR row of key tiles
+// Both product kernels stage 64-row chunks with direct global -> LDS copies
+// (row-major, XOR-swizzled; rows past N read as zeros, which contribute
+// exactly zero to every product here) and read transposed operands with the
+// gfx950 transposing LDS load, so each operand is staged once.
 #include <hip/hip_runtime.h>
 
 #include "device_common.h"
 #include "kernels.h"
+
+#ifndef RADIAL_BWD_XCD_BLOCK
+#define RADIAL_BWD_XCD_BLOCK 16  // tiles per XCD block (see xcd_remap)
+#endif
 
 namespace radial {
 
@@ -48,23 +56,30 @@ __global__ __launch_bounds__(256) void radial_bwd_pre_kernel(const bf16 *__restr
 // ---------------------------------------------------------------------------
 // 2. dK, dV: workgroup per (batch*head, key tile).  Wave w owns keys
 //    [32w, 32w + 32) of the tile, with K and V rows held as B operands.
-//    Query rows are staged MC at a time, row-major (A operand of S = Q K^T
-//    and dP = dO V^T) and transposed (A operand of dK^T = Q^T dS and
-//    dV^T = dO^T P).  S and dP come out with one key per lane column, so P
-//    and dS feed the next products as B operands without lane exchange.
+//    Query rows arrive in chunks of MC (Q, dO, LSE, Delta), triple buffered.
+//    Per 32-query block: S = Q K^T and dP = dO V^T read Q and dO row-major;
+//    S and dP come out with one key per lane column, so P and dS feed
+//    dV^T += dO^T P and dK^T += Q^T dS as B operands without lane exchange,
+//    and dO^T, Q^T are read with transposing loads.
 // ---------------------------------------------------------------------------
-template <int D, int T, int MC>
+template <int D, int T>
 struct DkdvCfg {
   static constexpr int NW = T / 32;
   static constexpr int NT = NW * 64;
+  static constexpr int MC = 64;          // query rows per chunk
+  static constexpr int NMB = MC / 32;
+  static constexpr int CPT = T / MC;     // chunks per query tile
   static constexpr int NKK = D / 16;
   static constexpr int NDB = D / 32;
-  static constexpr int NMB = MC / 32;
-  static constexpr int RS = D + 8;   // row-major stride (elements)
-  static constexpr int TS = MC + 4;  // transposed stride (elements)
+  static constexpr int NBUF = 3;         // chunk buffers (copies run two ahead)
+  static constexpr int CHUNK = MC * D;   // elements of one staged operand
+  using Copier = TileCopier<D, MC, NW>;
+  static constexpr int LPW = MC / (4 * NW);  // lanes per wave copying row terms
+  static constexpr int NCOPY = 2 * Copier::NDMA + 2;  // copies per wave per chunk
+  static_assert(NCOPY < 16 && LPW >= 1, "copy counts");
 };
 
-template <int D, int T, int MC>
+template <int D, int T>
 __global__ __launch_bounds__(T / 32 * 64, 1) void radial_bwd_dkdv_kernel(
     const bf16 *__restrict__ Q, const bf16 *__restrict__ K, const bf16 *__restrict__ V,
     const bf16 *__restrict__ dO, const float *__restrict__ LSE,
@@ -72,18 +87,14 @@ __global__ __launch_bounds__(T / 32 * 64, 1) void radial_bwd_dkdv_kernel(
     const int32_t *__restrict__ col_ptr, const int32_t *__restrict__ row_idx,
     const int32_t *__restrict__ col_order, int32_t N, int32_t nb, int32_t n_work,
     float scale_log2, float scale) {
-  using C = DkdvCfg<D, T, MC>;
-  __shared__ __attribute__((aligned(16))) bf16 Qs[MC * C::RS];
-  __shared__ __attribute__((aligned(16))) bf16 dOs[MC * C::RS];
-  __shared__ __attribute__((aligned(16))) bf16 Qt[D * C::TS];
-  __shared__ __attribute__((aligned(16))) bf16 dOt[D * C::TS];
-  __shared__ __attribute__((aligned(16))) float lse_s[MC];
-  __shared__ __attribute__((aligned(16))) float dl_s[MC];
+  using C = DkdvCfg<D, T>;
+  __shared__ __attribute__((aligned(1024))) bf16 lds_t[C::NBUF * 2 * C::CHUNK];
+  __shared__ __attribute__((aligned(16))) float lds_r[C::NBUF * 2 * C::MC];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int c32 = lane & 31, g = lane >> 5;
-  const int work = xcd_remap(blockIdx.x, n_work, 0);
+  const int work = xcd_remap(blockIdx.x, n_work, RADIAL_BWD_XCD_BLOCK);
   const int bh = work / nb;
   const int v = col_order[work - bh * nb];
   const int64_t base = (int64_t)bh * N * D;
@@ -106,61 +117,104 @@ __global__ __launch_bounds__(T / 32 * 64, 1) void radial_bwd_dkdv_kernel(
     adv[db] = zero16();
   }
 
+  // chunk list: every MC-row chunk of every query tile of the column, minus
+  // the chunks of the last query tile at or past N
   const int t_begin = col_ptr[v], t_end = col_ptr[v + 1];
-  for (int t = t_begin; t < t_end; ++t) {
-    const int u = row_idx[t];
-#pragma unroll 1
-    for (int c = 0; c < T / MC; ++c) {
-      const int m0 = u * T + c * MC;
-      const int valid = N - m0;
-      if (valid <= 0) break;
-      __syncthreads();
-      load_rows<MC, D, C::RS, C::NT>(Qs, Qb + (int64_t)m0 * D, valid, tid);
-      load_rows<MC, D, C::RS, C::NT>(dOs, dOb + (int64_t)m0 * D, valid, tid);
-      load_rows_t<MC, D, C::TS, C::NT>(Qt, Qb + (int64_t)m0 * D, valid, tid);
-      load_rows_t<MC, D, C::TS, C::NT>(dOt, dOb + (int64_t)m0 * D, valid, tid);
-      if (tid < MC) {
-        lse_s[tid] = tid < valid ? LSE[rbase + m0 + tid] * kLog2e : INFINITY;
-        dl_s[tid] = tid < valid ? Delta[rbase + m0 + tid] : 0.f;
+  int nch = (t_end - t_begin) * C::CPT;
+  if (t_end > t_begin && row_idx[t_end - 1] == nb - 1)
+    nch -= C::CPT - (N - (nb - 1) * T + C::MC - 1) / C::MC;
+  auto row0_of = [&](int c) { return row_idx[t_begin + c / C::CPT] * T + (c % C::CPT) * C::MC; };
+
+  typename C::Copier cp;
+  cp.init(wave, lane);
+  auto issue = [&](int c, int m0) {
+    const int buf = c % C::NBUF;
+    bf16 *qd = lds_t + buf * 2 * C::CHUNK;
+    cp.copy(qd, Qb + (int64_t)m0 * D, N - m0, wave);
+    cp.copy(qd + C::CHUNK, dOb + (int64_t)m0 * D, N - m0, wave);
+    // row terms: wave w copies floats [w * 4 LPW, (w + 1) * 4 LPW) of each
+    float *rd = lds_r + buf * 2 * C::MC + wave * 4 * C::LPW;
+    const auto rl = make_rsrc(LSE + rbase + m0, (N - m0) * 4);
+    const auto rdl = make_rsrc(Delta + rbase + m0, (N - m0) * 4);
+    if (lane < C::LPW) {
+      dma16b(rl, rd, (wave * 4 * C::LPW + 4 * lane) * 4);
+      dma16b(rdl, rd + C::MC, (wave * 4 * C::LPW + 4 * lane) * 4);
+    }
+  };
+
+  int row_a = nch > 0 ? row0_of(0) : 0;  // first rows of chunks c, c + 1, c + 2
+  int row_b = nch > 1 ? row0_of(1) : 0;
+  int row_c = nch > 2 ? row0_of(2) : 0;
+  if (nch > 0) issue(0, row_a);
+  if (nch > 1) {
+    issue(1, row_b);
+    wait_vmem_n<C::NCOPY>();
+  } else {
+    wait_vmem();
+  }
+  __syncthreads();
+
+  for (int c = 0; c < nch; ++c) {
+    if (c + 2 < nch) issue(c + 2, row_c);
+    const int next3 = c + 3 < nch ? row0_of(c + 3) : 0;
+    const int buf = c % C::NBUF;
+    const bf16 *Qs = lds_t + buf * 2 * C::CHUNK;
+    const bf16 *dOs = Qs + C::CHUNK;
+    const float *lse_s = lds_r + buf * 2 * C::MC;
+    const float *dl_s = lse_s + C::MC;
+
+#pragma unroll
+    for (int mb = 0; mb < C::NMB; ++mb) {
+      // S = Q K^T and dP = dO V^T for query rows mb*32 .. +32 of the chunk
+      bf16x8 qa[C::NKK], da[C::NKK];
+#pragma unroll
+      for (int kk = 0; kk < C::NKK; ++kk) {
+        qa[kk] = ld8(Qs + swz<D>(mb * 32 + c32, 2 * kk + g));
+        da[kk] = ld8(dOs + swz<D>(mb * 32 + c32, 2 * kk + g));
       }
-      __syncthreads();
-
+      f32x16 s = zero16(), dp = zero16();
 #pragma unroll
-      for (int mb = 0; mb < C::NMB; ++mb) {
-        f32x16 s = zero16(), dp = zero16();
+      for (int kk = 0; kk < C::NKK; ++kk) {
+        s = mfma32(qa[kk], kf[kk], s);
+        dp = mfma32(da[kk], vf[kk], dp);
+      }
+      // register r holds query row mb*32 + 8*(r/4) + 4g + r%4 of this key
+      bf16x8 pb[2], dsb[2];
 #pragma unroll
-        for (int kk = 0; kk < C::NKK; ++kk)
-          s = mfma32(ld8(&Qs[(mb * 32 + c32) * C::RS + kk * 16 + g * 8]), kf[kk], s);
+      for (int i = 0; i < 4; ++i) {
+        const f32x4 l4 = *reinterpret_cast<const f32x4 *>(&lse_s[mb * 32 + 8 * i + 4 * g]);
+        const f32x4 d4 = *reinterpret_cast<const f32x4 *>(&dl_s[mb * 32 + 8 * i + 4 * g]);
 #pragma unroll
-        for (int kk = 0; kk < C::NKK; ++kk)
-          dp = mfma32(ld8(&dOs[(mb * 32 + c32) * C::RS + kk * 16 + g * 8]), vf[kk], dp);
-
-        bf16x8 pb[2], dsb[2];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const f32x4 l4 = *reinterpret_cast<const f32x4 *>(&lse_s[mb * 32 + 8 * i + 4 * g]);
-          const f32x4 d4 = *reinterpret_cast<const f32x4 *>(&dl_s[mb * 32 + 8 * i + 4 * g]);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int r = 4 * i + j;
-            const float p = fast_exp2(s[r] * scale_log2 - l4[j]);
-            const float ds = p * (dp[r] - d4[j]);
-            pb[r >> 3][r & 7] = bf16(p);
-            dsb[r >> 3][r & 7] = bf16(ds);
-          }
+        for (int jj = 0; jj < 4; ++jj) {
+          const int r = 4 * i + jj;
+          const float p = fast_exp2(fmaf(s[r], scale_log2, -l4[jj] * kLog2e));
+          pb[r >> 3][r & 7] = bf16(p);
+          dsb[r >> 3][r & 7] = bf16(p * (dp[r] - d4[jj]));
         }
+      }
+      // dV^T += dO^T P and dK^T += Q^T dS
 #pragma unroll
-        for (int db = 0; db < C::NDB; ++db) {
+      for (int db = 0; db < C::NDB; ++db) {
 #pragma unroll
-          for (int ks = 0; ks < 2; ++ks) {
-            const int off = (db * 32 + c32) * C::TS + mb * 32 + ks * 16 + 4 * g;
-            adv[db] = mfma32(ld_perm(&dOt[off]), pb[ks], adv[db]);
-            adk[db] = mfma32(ld_perm(&Qt[off]), dsb[ks], adk[db]);
-          }
+        for (int ks = 0; ks < 2; ++ks) {
+          adv[db] = mfma32(ld_trA<D>(dOs, db, mb, ks, lane), pb[ks], adv[db]);
+          adk[db] = mfma32(ld_trA<D>(Qs, db, mb, ks, lane), dsb[ks], adk[db]);
         }
       }
     }
+
+    if (c + 1 < nch) {  // chunk c + 1 has landed (c + 2 may be in flight)
+      if (c + 2 < nch)
+        wait_vmem_n<C::NCOPY>();
+      else
+        wait_vmem();
+    }
+    __syncthreads();
+    row_a = row_b;
+    row_b = row_c;
+    row_c = next3;
   }
+  (void)row_a;
 
   if (k_ok) {
     bf16 *dkrow = dK + base + (int64_t)key * D;
@@ -171,9 +225,9 @@ __global__ __launch_bounds__(T / 32 * 64, 1) void radial_bwd_dkdv_kernel(
       for (int i = 0; i < 4; ++i) {
         bf16x4 ok4, ov4;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          ok4[j] = bf16(adk[db][4 * i + j] * scale);
-          ov4[j] = bf16(adv[db][4 * i + j]);
+        for (int jj = 0; jj < 4; ++jj) {
+          ok4[jj] = bf16(adk[db][4 * i + jj] * scale);
+          ov4[jj] = bf16(adv[db][4 * i + jj]);
         }
         st4(dkrow + db * 32 + 8 * i + 4 * g, ok4);
         st4(dvrow + db * 32 + 8 * i + 4 * g, ov4);
@@ -184,37 +238,38 @@ __global__ __launch_bounds__(T / 32 * 64, 1) void radial_bwd_dkdv_kernel(
 
 // ---------------------------------------------------------------------------
 // 3. dQ: workgroup per (batch*head, query tile).  Wave w owns queries
-//    [32w, 32w + 32), with Q and dO rows held as B operands.  Key tiles are
-//    staged KC keys at a time: K and V row-major (A operands of S^T = K Q^T
-//    and dP^T = V dO^T) and K transposed (A operand of dQ^T = K^T dS^T).
+//    [32w, 32w + 32), with Q and dO rows held as B operands and the lane's
+//    LSE and Delta in registers.  Key chunks of KC rows (K, V) are double
+//    buffered: S^T = K Q^T and dP^T = V dO^T read K and V row-major, and
+//    dQ^T += K^T dS^T reads K^T with transposing loads.
 // ---------------------------------------------------------------------------
-template <int D, int T, int KC>
+template <int D, int T>
 struct DqCfg {
   static constexpr int NW = T / 32;
   static constexpr int NT = NW * 64;
+  static constexpr int KC = 64;
+  static constexpr int CPT = T / KC;
+  static constexpr int NKB = KC / 32;
   static constexpr int NKK = D / 16;
   static constexpr int NDB = D / 32;
-  static constexpr int NKB = KC / 32;
-  static constexpr int RS = D + 8;
-  static constexpr int TS = KC + 4;
+  static constexpr int CHUNK = KC * D;
+  using Copier = TileCopier<D, KC, NW>;
 };
 
-template <int D, int T, int KC>
+template <int D, int T>
 __global__ __launch_bounds__(T / 32 * 64, 2) void radial_bwd_dq_kernel(
     const bf16 *__restrict__ Q, const bf16 *__restrict__ K, const bf16 *__restrict__ V,
     const bf16 *__restrict__ dO, const float *__restrict__ LSE,
     const float *__restrict__ Delta, bf16 *__restrict__ dQ,
     const int32_t *__restrict__ row_ptr, const int32_t *__restrict__ col_idx, int32_t N,
     int32_t nb, int32_t n_work, float scale_log2, float scale) {
-  using C = DqCfg<D, T, KC>;
-  __shared__ __attribute__((aligned(16))) bf16 Ks[KC * C::RS];
-  __shared__ __attribute__((aligned(16))) bf16 Vs[KC * C::RS];
-  __shared__ __attribute__((aligned(16))) bf16 Kt[D * C::TS];
+  using C = DqCfg<D, T>;
+  __shared__ __attribute__((aligned(1024))) bf16 lds[4 * C::CHUNK];  // K0 V0 K1 V1
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int c32 = lane & 31, g = lane >> 5;
-  const int work = xcd_remap(blockIdx.x, n_work, 0);
+  const int work = xcd_remap(blockIdx.x, n_work, RADIAL_BWD_XCD_BLOCK);
   const int bh = work / nb;
   const int u = work - bh * nb;
   const int64_t base = (int64_t)bh * N * D;
@@ -229,7 +284,8 @@ __global__ __launch_bounds__(T / 32 * 64, 2) void radial_bwd_dq_kernel(
     qf[kk] = q_ok ? ld8(Q + base + (int64_t)qrow * D + kk * 16 + g * 8) : zero_bf16x8();
     dof[kk] = q_ok ? ld8(dO + base + (int64_t)qrow * D + kk * 16 + g * 8) : zero_bf16x8();
   }
-  const float lse2 = q_ok ? LSE[(int64_t)bh * N + qrow] * kLog2e : INFINITY;
+  // rows past N: Q, dO are zero and LSE, Delta are taken as 0, so dS = 0
+  const float lse2 = q_ok ? LSE[(int64_t)bh * N + qrow] * kLog2e : 0.f;
   const float dl = q_ok ? Delta[(int64_t)bh * N + qrow] : 0.f;
 
   f32x16 adq[C::NDB];
@@ -237,45 +293,65 @@ __global__ __launch_bounds__(T / 32 * 64, 2) void radial_bwd_dq_kernel(
   for (int db = 0; db < C::NDB; ++db) adq[db] = zero16();
 
   const int t_begin = row_ptr[u], t_end = row_ptr[u + 1];
-  for (int t = t_begin; t < t_end; ++t) {
-    const int k0 = col_idx[t] * T;
-#pragma unroll 1
-    for (int c = 0; c < T / KC; ++c) {
-      const int kc0 = k0 + c * KC;
-      const int valid = N - kc0;
-      if (valid <= 0) break;
-      __syncthreads();
-      load_rows<KC, D, C::RS, C::NT>(Ks, Kb + (int64_t)kc0 * D, valid, tid);
-      load_rows<KC, D, C::RS, C::NT>(Vs, Vb + (int64_t)kc0 * D, valid, tid);
-      load_rows_t<KC, D, C::TS, C::NT>(Kt, Kb + (int64_t)kc0 * D, valid, tid);
-      __syncthreads();
+  int nch = (t_end - t_begin) * C::CPT;
+  if (t_end > t_begin && col_idx[t_end - 1] == nb - 1)
+    nch -= C::CPT - (N - (nb - 1) * T + C::KC - 1) / C::KC;
+  auto key_of = [&](int c) { return col_idx[t_begin + c / C::CPT] * T + (c % C::CPT) * C::KC; };
+
+  typename C::Copier cp;
+  cp.init(wave, lane);
+  auto issue = [&](int c, int k0) {
+    bf16 *kd = lds + (c & 1) * 2 * C::CHUNK;
+    cp.copy(kd, Kb + (int64_t)k0 * D, N - k0, wave);
+    cp.copy(kd + C::CHUNK, Vb + (int64_t)k0 * D, N - k0, wave);
+  };
+
+  int key_n = nch > 0 ? key_of(0) : 0;   // first keys of chunks c and c + 1
+  int key_nn = nch > 1 ? key_of(1) : 0;
+  if (nch > 0) issue(0, key_n);
+  wait_vmem();  // Q, dO fragments, LSE, Delta and the first chunk
+  __syncthreads();
+
+  for (int c = 0; c < nch; ++c) {
+    if (c + 1 < nch) issue(c + 1, key_nn);  // lands during this chunk
+    const int key_3 = c + 2 < nch ? key_of(c + 2) : 0;
+    const bf16 *Ks = lds + (c & 1) * 2 * C::CHUNK;
+    const bf16 *Vs = Ks + C::CHUNK;
 
 #pragma unroll
-      for (int kb = 0; kb < C::NKB; ++kb) {
-        f32x16 s = zero16(), dp = zero16();
+    for (int kb = 0; kb < C::NKB; ++kb) {
+      bf16x8 ka[C::NKK], va[C::NKK];
 #pragma unroll
-        for (int kk = 0; kk < C::NKK; ++kk)
-          s = mfma32(ld8(&Ks[(kb * 32 + c32) * C::RS + kk * 16 + g * 8]), qf[kk], s);
-#pragma unroll
-        for (int kk = 0; kk < C::NKK; ++kk)
-          dp = mfma32(ld8(&Vs[(kb * 32 + c32) * C::RS + kk * 16 + g * 8]), dof[kk], dp);
-        bf16x8 dsb[2];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int kr = kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-          const float p = kr < valid ? fast_exp2(s[r] * scale_log2 - lse2) : 0.f;
-          dsb[r >> 3][r & 7] = bf16(p * (dp[r] - dl));
-        }
-#pragma unroll
-        for (int db = 0; db < C::NDB; ++db) {
-#pragma unroll
-          for (int ks = 0; ks < 2; ++ks)
-            adq[db] = mfma32(ld_perm(&Kt[(db * 32 + c32) * C::TS + kb * 32 + ks * 16 + 4 * g]),
-                             dsb[ks], adq[db]);
-        }
+      for (int kk = 0; kk < C::NKK; ++kk) {
+        ka[kk] = ld8(Ks + swz<D>(kb * 32 + c32, 2 * kk + g));
+        va[kk] = ld8(Vs + swz<D>(kb * 32 + c32, 2 * kk + g));
       }
+      f32x16 s = zero16(), dp = zero16();
+#pragma unroll
+      for (int kk = 0; kk < C::NKK; ++kk) {
+        s = mfma32(ka[kk], qf[kk], s);
+        dp = mfma32(va[kk], dof[kk], dp);
+      }
+      // register r holds key kb*32 + 8*(r/4) + 4g + r%4 of the chunk
+      bf16x8 dsb[2];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = fast_exp2(fmaf(s[r], scale_log2, -lse2));
+        dsb[r >> 3][r & 7] = bf16(p * (dp[r] - dl));
+      }
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+          adq[db] = mfma32(ld_trA<D>(Ks, db, kb, ks, lane), dsb[ks], adq[db]);
     }
+
+    wait_vmem();      // chunk c + 1 has landed here ...
+    __syncthreads();  // ... and everywhere; chunk c is no longer read
+    key_n = key_nn;
+    key_nn = key_3;
   }
+  (void)key_n;
 
   if (q_ok) {
     bf16 *row = dQ + base + (int64_t)qrow * D;
@@ -285,7 +361,7 @@ __global__ __launch_bounds__(T / 32 * 64, 2) void radial_bwd_dq_kernel(
       for (int i = 0; i < 4; ++i) {
         bf16x4 o4;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) o4[j] = bf16(adq[db][4 * i + j] * scale);
+        for (int jj = 0; jj < 4; ++jj) o4[jj] = bf16(adq[db][4 * i + jj] * scale);
         st4(row + db * 32 + 8 * i + 4 * g, o4);
       }
     }
@@ -294,7 +370,6 @@ __global__ __launch_bounds__(T / 32 * 64, 2) void radial_bwd_dq_kernel(
 
 template <int D, int T>
 hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t stream) {
-  constexpr int MC = 64, KC = 64;
   const int64_t rows = (int64_t)a.BH * a.N;
   constexpr int RPB = 256 / (D / 8);
   hipLaunchKernelGGL((radial_bwd_pre_kernel<D>), dim3((unsigned)((rows + RPB - 1) / RPB)),
@@ -304,17 +379,17 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t stream) {
   if (e != hipSuccess) return e;
   const int64_t works = (int64_t)a.BH * a.nb;
   const float sl2 = a.scale * kLog2e;
-  hipLaunchKernelGGL((radial_bwd_dkdv_kernel<D, T, MC>), dim3((unsigned)works),
-                     dim3(DkdvCfg<D, T, MC>::NT), 0, stream, (const bf16 *)a.q,
-                     (const bf16 *)a.k, (const bf16 *)a.v, (const bf16 *)a.dout, a.lse, a.delta,
-                     (bf16 *)a.dk, (bf16 *)a.dv, a.col_ptr, a.row_idx, a.col_order, a.N, a.nb,
-                     (int32_t)works, sl2, a.scale);
+  hipLaunchKernelGGL((radial_bwd_dkdv_kernel<D, T>), dim3((unsigned)works),
+                     dim3(DkdvCfg<D, T>::NT), 0, stream, (const bf16 *)a.q, (const bf16 *)a.k,
+                     (const bf16 *)a.v, (const bf16 *)a.dout, a.lse, a.delta, (bf16 *)a.dk,
+                     (bf16 *)a.dv, a.col_ptr, a.row_idx, a.col_order, a.N, a.nb, (int32_t)works,
+                     sl2, a.scale);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((radial_bwd_dq_kernel<D, T, KC>), dim3((unsigned)works),
-                     dim3(DqCfg<D, T, KC>::NT), 0, stream, (const bf16 *)a.q, (const bf16 *)a.k,
-                     (const bf16 *)a.v, (const bf16 *)a.dout, a.lse, a.delta, (bf16 *)a.dq,
-                     a.row_ptr, a.col_idx, a.N, a.nb, (int32_t)works, sl2, a.scale);
+  hipLaunchKernelGGL((radial_bwd_dq_kernel<D, T>), dim3((unsigned)works), dim3(DqCfg<D, T>::NT),
+                     0, stream, (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.v,
+                     (const bf16 *)a.dout, a.lse, a.delta, (bf16 *)a.dq, a.row_ptr, a.col_idx,
+                     a.N, a.nb, (int32_t)works, sl2, a.scale);
   return hipGetLastError();
 }
 

@@ -138,8 +138,62 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, bf16 *lds_block,
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)lds_block, 16, byte_off, 0, 0, 0);
 }
 
+// Byte-addressed variant for non-bf16 LDS data (e.g. fp32 row terms).
+__device__ __forceinline__ void dma16b(__amdgpu_buffer_rsrc_t r, void *lds_block, int byte_off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)lds_block, 16, byte_off, 0, 0, 0);
+}
+
+// Copies a ROWS x D bf16 tile (row-major at `src`, `valid` rows before the
+// end of the sequence) into a row-major, swizzled LDS tile, NW waves sharing
+// the work: copy jj of wave w fills LDS bytes [(w*NDMA + jj) * 1024, +1024);
+// lane l writes element e = blk*512 + 8l, i.e. row e / D and physical 16-byte
+// block (e % D) / 8, which holds logical block (physical ^ swz_f(row)) of the
+// row.  Rows at or past `valid` read as zeros.
+template <int D, int ROWS, int NW>
+struct TileCopier {
+  static constexpr int NDMA = ROWS * D * 2 / 1024 / NW;  // copies per wave
+  static_assert(NDMA >= 1 && ROWS * D * 2 % (1024 * NW) == 0, "tile split");
+  int off[NDMA];
+  __device__ __forceinline__ void init(int wave, int lane);
+  __device__ __forceinline__ void copy(bf16 *dst, const bf16 *src, int valid, int wave) const {
+    const auto r = make_rsrc(src, valid * D * 2);
+#pragma unroll
+    for (int jj = 0; jj < NDMA; ++jj) dma16(r, dst + (wave * NDMA + jj) * 512, off[jj]);
+  }
+};
+
+// A operand (32 x 16) of a product contracting over the rows of a row-major
+// swizzled [rows][D] LDS tile, for output rows d = 32 db + (lane % 32) and
+// contraction rows 32 rb + 16 ks + (the permuted K assignment), read with
+// two transposing loads.
+template <int D>
+__device__ __forceinline__ bf16x8 ld_trA(const bf16 *tile, int db, int rb, int ks, int lane) {
+  const int j = lane & 15, G = lane >> 4;
+  const int col = db * 32 + 16 * (G & 1) + 4 * (j & 3);
+  const int r0 = rb * 32 + ks * 16 + 4 * (G >> 1) + (j >> 2);
+  return cat(ld_tr(tile + swz<D>(r0, col >> 3) + (col & 7)),
+             ld_tr(tile + swz<D>(r0 + 8, col >> 3) + (col & 7)));
+}
+
 // s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maximum)
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+template <int D, int ROWS, int NW>
+__device__ __forceinline__ void TileCopier<D, ROWS, NW>::init(int wave, int lane) {
+#pragma unroll
+  for (int jj = 0; jj < NDMA; ++jj) {
+    const int e = (wave * NDMA + jj) * 512 + 8 * lane;
+    const int row = e / D, pblk = (e % D) / 8;
+    off[jj] = row * D * 2 + 16 * (pblk ^ swz_f<D>(row));
+  }
+}
+
+// s_waitcnt vmcnt(n) for a compile-time n < 16
+template <int n>
+__device__ __forceinline__ void wait_vmem_n() {
+  static_assert(n >= 0 && n < 16, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | n);
+}
 
 // Work-item order for a launch of n workgroups whose work items are
 // numbered head-major (query tile fastest).  The hardware hands workgroups to
