@@ -111,7 +111,7 @@ def cpu_baseline(w, layout_kept, budget_s: float = 15.0):
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:
         threads = os.cpu_count() or 1
-    q, k, v = workloads.make_inputs(w.B, w.H, w.N, w.D, w.seed, heads=[0])
+    q, k, v = workloads.workload_inputs(w, with_dout=False, heads=[0])
     qh, kh, vh = (t[0, 0].to(torch.float64).numpy() for t in (q, k, v))
     nb = layout_kept.shape[0]
     sizes = np.full(nb, w.T)

@@ -56,27 +56,39 @@ __global__ __launch_bounds__(256) void radial_bwd_pre_kernel(const bf16 *__restr
 // ---------------------------------------------------------------------------
 // 2. dK, dV: workgroup per (batch*head, key tile).  Wave w owns keys
 //    [32w, 32w + 32) of the tile, with K and V rows held as B operands.
-//    Query rows arrive in chunks of MC (Q, dO, LSE, Delta), triple buffered.
-//    Per 32-query block: S = Q K^T and dP = dO V^T read Q and dO row-major;
-//    S and dP come out with one key per lane column, so P and dS feed
-//    dV^T += dO^T P and dK^T += Q^T dS as B operands without lane exchange,
-//    and dO^T, Q^T are read with transposing loads.
+//    Query rows arrive in chunks of MC = 64 (Q, dO, LSE, Delta) in four LDS
+//    buffers.  Each 32-query block j goes through three stages:
+//      1. S = Q K^T and dP = dO V^T        (matrix cores; Q, dO row-major)
+//      2. P = exp(scale S - LSE), dS = P (dP - Delta)   (vector ALU)
+//      3. dV^T += dO^T P, dK^T += Q^T dS   (matrix cores; dO^T, Q^T read
+//                                           with transposing loads)
+//    S and dP come out with one key per lane column, so P and dS feed stage 3
+//    as B operands without lane exchange.  The stages are software pipelined:
+//    step j runs stage 3 of block j - 2, stage 2 of block j - 1 and stage 1
+//    of block j in one basic block, so the vector work of one block overlaps
+//    the products of two others within the wave (one wave per SIMD here).
+//    Step pairs form a chunk iteration c, which reads chunks c and c - 1 while
+//    the copies of chunk c + 2 are in flight.
 // ---------------------------------------------------------------------------
 template <int D, int T>
 struct DkdvCfg {
   static constexpr int NW = T / 32;
   static constexpr int NT = NW * 64;
   static constexpr int MC = 64;          // query rows per chunk
-  static constexpr int NMB = MC / 32;
   static constexpr int CPT = T / MC;     // chunks per query tile
   static constexpr int NKK = D / 16;
   static constexpr int NDB = D / 32;
-  static constexpr int NBUF = 3;         // chunk buffers (copies run two ahead)
+  static constexpr int NBUF = 4;         // chunk buffers
   static constexpr int CHUNK = MC * D;   // elements of one staged operand
   using Copier = TileCopier<D, MC, NW>;
   static constexpr int LPW = MC / (4 * NW);  // lanes per wave copying row terms
   static constexpr int NCOPY = 2 * Copier::NDMA + 2;  // copies per wave per chunk
   static_assert(NCOPY < 16 && LPW >= 1, "copy counts");
+};
+
+template <int V>
+struct BwdFlag {
+  static constexpr int value = V;
 };
 
 template <int D, int T>
@@ -88,8 +100,9 @@ __global__ __launch_bounds__(T / 32 * 64, 1) void radial_bwd_dkdv_kernel(
     const int32_t *__restrict__ col_order, int32_t N, int32_t nb, int32_t n_work,
     float scale_log2, float scale) {
   using C = DkdvCfg<D, T>;
-  __shared__ __attribute__((aligned(1024))) bf16 lds_t[C::NBUF * 2 * C::CHUNK];
-  __shared__ __attribute__((aligned(16))) float lds_r[C::NBUF * 2 * C::MC];
+  constexpr int NB = C::NBUF;
+  __shared__ __attribute__((aligned(1024))) bf16 lds_t[NB * 2 * C::CHUNK];
+  __shared__ __attribute__((aligned(16))) float lds_r[NB * 2 * C::MC];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -127,24 +140,126 @@ __global__ __launch_bounds__(T / 32 * 64, 1) void radial_bwd_dkdv_kernel(
 
   typename C::Copier cp;
   cp.init(wave, lane);
+  // copies of chunk c (first row m0) into buffer c % NB; issued from inline
+  // assembly (see dma16_async), so every wait below is explicit
   auto issue = [&](int c, int m0) {
-    const int buf = c % C::NBUF;
+    const int buf = c % NB;
     bf16 *qd = lds_t + buf * 2 * C::CHUNK;
-    cp.copy(qd, Qb + (int64_t)m0 * D, N - m0, wave);
-    cp.copy(qd + C::CHUNK, dOb + (int64_t)m0 * D, N - m0, wave);
+    cp.copy_async(qd, Qb + (int64_t)m0 * D, N - m0, wave);
+    cp.copy_async(qd + C::CHUNK, dOb + (int64_t)m0 * D, N - m0, wave);
     // row terms: wave w copies floats [w * 4 LPW, (w + 1) * 4 LPW) of each
     float *rd = lds_r + buf * 2 * C::MC + wave * 4 * C::LPW;
-    const auto rl = make_rsrc(LSE + rbase + m0, (N - m0) * 4);
-    const auto rdl = make_rsrc(Delta + rbase + m0, (N - m0) * 4);
+    const u32x4 rl = rsrc_words(LSE + rbase + m0, (N - m0) * 4);
+    const u32x4 rdl = rsrc_words(Delta + rbase + m0, (N - m0) * 4);
     if (lane < C::LPW) {
-      dma16b(rl, rd, (wave * 4 * C::LPW + 4 * lane) * 4);
-      dma16b(rdl, rd + C::MC, (wave * 4 * C::LPW + 4 * lane) * 4);
+      dma16b_async(rl, rd, (wave * 4 * C::LPW + 4 * lane) * 4);
+      dma16b_async(rdl, rd + C::MC, (wave * 4 * C::LPW + 4 * lane) * 4);
     }
   };
 
-  int row_a = nch > 0 ? row0_of(0) : 0;  // first rows of chunks c, c + 1, c + 2
+  // stage-1 results of a block: sd[0] = S, sd[1] = dP (register r holds
+  // query row 32 (j % 2) + 8 (r / 4) + 4 g + r % 4 of the chunk, for key
+  // column c32), and the LSE (rt[0..3]) and Delta (rt[4..7]) of those rows
+  struct Blk {
+    f32x16 sd[2];
+    f32x4 rt[8];
+  };
+  // stage 1 of block j
+  auto stage1 = [&](int j, Blk &b) {
+    const int buf = (j >> 1) % NB, mb = j & 1;
+    const bf16 *Qs = lds_t + buf * 2 * C::CHUNK;
+    const bf16 *dOs = Qs + C::CHUNK;
+#pragma unroll
+    for (int kk = 0; kk < C::NKK; ++kk) {
+      const bf16x8 qa = ld8(Qs + swz<D>(mb * 32 + c32, 2 * kk + g));
+      const bf16x8 da = ld8(dOs + swz<D>(mb * 32 + c32, 2 * kk + g));
+      b.sd[0] = mfma32(qa, kf[kk], kk == 0 ? zero16() : b.sd[0]);
+      b.sd[1] = mfma32(da, vf[kk], kk == 0 ? zero16() : b.sd[1]);
+    }
+    const float *lse_s = lds_r + buf * 2 * C::MC + 32 * mb;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      b.rt[i] = *reinterpret_cast<const f32x4 *>(&lse_s[8 * i + 4 * g]);
+      b.rt[4 + i] = *reinterpret_cast<const f32x4 *>(&lse_s[C::MC + 8 * i + 4 * g]);
+    }
+  };
+  // stage 2 of block j: pd[0] = P, pd[1] = dS, rounded to bf16
+  auto stage2 = [&](const Blk &b, bf16x8 (&pd)[2][2]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int r = 4 * i + jj;
+        const float p = fast_exp2(fmaf(b.sd[0][r], scale_log2, -b.rt[i][jj] * kLog2e));
+        pd[0][r >> 3][r & 7] = bf16(p);
+        pd[1][r >> 3][r & 7] = bf16(p * (b.sd[1][r] - b.rt[4 + i][jj]));
+      }
+    }
+  };
+  // stage 3 of block j: dV^T += dO^T P, dK^T += Q^T dS
+  auto stage3 = [&](int j, const bf16x8 (&pd)[2][2]) {
+    const bf16 *Qs = lds_t + ((j >> 1) % NB) * 2 * C::CHUNK;
+    const bf16 *dOs = Qs + C::CHUNK;
+    const int mb = j & 1;
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db) {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        adv[db] = mfma32(ld_trA<D>(dOs, db, mb, ks, lane), pd[0][ks], adv[db]);
+        adk[db] = mfma32(ld_trA<D>(Qs, db, mb, ks, lane), pd[1][ks], adk[db]);
+      }
+    }
+  };
+
+  // step j: stage 3 of j - 2, stage 2 of j - 1, stage 1 of j (as flagged)
+  auto step = [&](int j, auto F1, auto F2, auto F3, Blk &sd_new, const Blk &sd_old,
+                  bf16x8 (&pd_new)[2][2], const bf16x8 (&pd_old)[2][2]) {
+    constexpr bool s1 = decltype(F1)::value, s2 = decltype(F2)::value,
+                   s3 = decltype(F3)::value;
+    constexpr int NM = 4 * C::NDB;  // products per stage
+    if constexpr (s3) stage3(j - 2, pd_old);
+    if constexpr (s2) stage2(sd_old, pd_new);
+    if constexpr (s1) stage1(j, sd_new);
+    // per product: its operand reads run ahead and a few vector-ALU
+    // instructions of stage 2 go along
+    // (0x008 products, 0x100 LDS reads, 0x002 vector ALU, 0x400 exp2)
+    if constexpr (s3) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int i = 0; i < NM; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        if constexpr (s2) {
+          __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+          if (i % 2 == 0) __builtin_amdgcn_sched_group_barrier(0x400, 1, 0);
+        }
+      }
+    }
+    if constexpr (s1) {
+#pragma unroll
+      for (int i = 0; i < NM; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        if constexpr (s2) {
+          __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+          if (i % 2 == 0) __builtin_amdgcn_sched_group_barrier(0x400, 1, 0);
+        }
+      }
+    }
+    // keeps stage 2 in this block (otherwise it may be sunk past the chunk
+    // end's branches, away from the products it overlaps with)
+    if constexpr (s2)
+      asm volatile("" ::"v"(pd_new[0][0]), "v"(pd_new[0][1]), "v"(pd_new[1][0]),
+                   "v"(pd_new[1][1]));
+  };
+
+  Blk sdA, sdB;                     // stage-1 results of even / odd blocks
+  bf16x8 pdA[2][2], pdB[2][2];      // stage-2 results of even / odd blocks
+  const BwdFlag<0> NO;
+  const BwdFlag<1> YES;
+
+  int row_a = nch > 0 ? row0_of(0) : 0;  // first rows of chunks c + 1, c + 2
   int row_b = nch > 1 ? row0_of(1) : 0;
-  int row_c = nch > 2 ? row0_of(2) : 0;
   if (nch > 0) issue(0, row_a);
   if (nch > 1) {
     issue(1, row_b);
@@ -153,68 +268,37 @@ __global__ __launch_bounds__(T / 32 * 64, 1) void radial_bwd_dkdv_kernel(
     wait_vmem();
   }
   __syncthreads();
+  int row_c = nch > 2 ? row0_of(2) : 0;
 
-  for (int c = 0; c < nch; ++c) {
-    if (c + 2 < nch) issue(c + 2, row_c);
-    const int next3 = c + 3 < nch ? row0_of(c + 3) : 0;
-    const int buf = c % C::NBUF;
-    const bf16 *Qs = lds_t + buf * 2 * C::CHUNK;
-    const bf16 *dOs = Qs + C::CHUNK;
-    const float *lse_s = lds_r + buf * 2 * C::MC;
-    const float *dl_s = lse_s + C::MC;
-
-#pragma unroll
-    for (int mb = 0; mb < C::NMB; ++mb) {
-      // S = Q K^T and dP = dO V^T for query rows mb*32 .. +32 of the chunk
-      bf16x8 qa[C::NKK], da[C::NKK];
-#pragma unroll
-      for (int kk = 0; kk < C::NKK; ++kk) {
-        qa[kk] = ld8(Qs + swz<D>(mb * 32 + c32, 2 * kk + g));
-        da[kk] = ld8(dOs + swz<D>(mb * 32 + c32, 2 * kk + g));
-      }
-      f32x16 s = zero16(), dp = zero16();
-#pragma unroll
-      for (int kk = 0; kk < C::NKK; ++kk) {
-        s = mfma32(qa[kk], kf[kk], s);
-        dp = mfma32(da[kk], vf[kk], dp);
-      }
-      // register r holds query row mb*32 + 8*(r/4) + 4g + r%4 of this key
-      bf16x8 pb[2], dsb[2];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const f32x4 l4 = *reinterpret_cast<const f32x4 *>(&lse_s[mb * 32 + 8 * i + 4 * g]);
-        const f32x4 d4 = *reinterpret_cast<const f32x4 *>(&dl_s[mb * 32 + 8 * i + 4 * g]);
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const int r = 4 * i + jj;
-          const float p = fast_exp2(fmaf(s[r], scale_log2, -l4[jj] * kLog2e));
-          pb[r >> 3][r & 7] = bf16(p);
-          dsb[r >> 3][r & 7] = bf16(p * (dp[r] - d4[jj]));
-        }
-      }
-      // dV^T += dO^T P and dK^T += Q^T dS
-#pragma unroll
-      for (int db = 0; db < C::NDB; ++db) {
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          adv[db] = mfma32(ld_trA<D>(dOs, db, mb, ks, lane), pb[ks], adv[db]);
-          adk[db] = mfma32(ld_trA<D>(Qs, db, mb, ks, lane), dsb[ks], adk[db]);
-        }
-      }
-    }
-
-    if (c + 1 < nch) {  // chunk c + 1 has landed (c + 2 may be in flight)
-      if (c + 2 < nch)
-        wait_vmem_n<C::NCOPY>();
-      else
-        wait_vmem();
-    }
+  // end of chunk iteration c: chunk c + 1 landed and visible (c + 2 may be
+  // in flight); the buffer of chunk c - 1 is free afterwards
+  auto chunk_end = [&](int c) {
+    if (c + 2 < nch)
+      wait_vmem_n<C::NCOPY>();
+    else
+      wait_vmem();
     __syncthreads();
-    row_a = row_b;
-    row_b = row_c;
-    row_c = next3;
+  };
+
+  if (nch > 0) {
+    // chunk iteration 0: steps 0 and 1
+    if (nch > 2) issue(2, row_c);
+    int row_d = nch > 3 ? row0_of(3) : 0;
+    step(0, YES, NO, NO, sdA, sdB, pdB, pdA);
+    step(1, YES, YES, NO, sdB, sdA, pdA, pdB);
+    chunk_end(0);
+    // chunk iterations 1 .. nch - 1: steps 2c, 2c + 1
+    for (int c = 1; c < nch; ++c) {
+      if (c + 2 < nch) issue(c + 2, row_d);
+      row_d = c + 3 < nch ? row0_of(c + 3) : 0;
+      step(2 * c, YES, YES, YES, sdA, sdB, pdB, pdA);
+      step(2 * c + 1, YES, YES, YES, sdB, sdA, pdA, pdB);
+      chunk_end(c);
+    }
+    // drain: steps 2 nch, 2 nch + 1
+    step(2 * nch, NO, YES, YES, sdA, sdB, pdB, pdA);
+    step(2 * nch + 1, NO, NO, YES, sdB, sdA, pdA, pdB);
   }
-  (void)row_a;
 
   if (k_ok) {
     bf16 *dkrow = dK + base + (int64_t)key * D;

@@ -143,12 +143,54 @@ __device__ __forceinline__ void dma16b(__amdgpu_buffer_rsrc_t r, void *lds_block
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)lds_block, 16, byte_off, 0, 0, 0);
 }
 
+typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
+
+// The four words of a raw buffer resource over `bytes` bytes at p, in
+// scalar registers (p and bytes must be wave-uniform).  Same layout as
+// make_rsrc: base, base high bits (stride 0), record count, format word.
+__device__ __forceinline__ u32x4 rsrc_words(const void *p, int bytes) {
+  const unsigned long long a = (unsigned long long)p;
+  u32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((unsigned)a);
+  r[1] = __builtin_amdgcn_readfirstlane((unsigned)(a >> 32) & 0xffffu);
+  r[2] = __builtin_amdgcn_readfirstlane((unsigned)bytes);
+  r[3] = 0x00020000u;
+  return r;
+}
+
+// dma16 issued from inline assembly.  The compiler does not see this copy,
+// so it adds no vmcnt waits of its own before LDS reads that it cannot prove
+// disjoint from the copy's destination (it cannot for the transposing reads,
+// and would otherwise make every copy complete before the next V^T read).
+// The caller therefore owns the wait: s_waitcnt vmcnt(0) (wait_vmem) and a
+// barrier before anyone reads the destination.  The instruction writes LDS
+// only (no register results), and M0, which carries the LDS address, is
+// restored afterwards.
+__device__ __forceinline__ void dma16_async(u32x4 r, const bf16 *lds_block, int byte_off) {
+  const unsigned lds_addr = __builtin_amdgcn_readfirstlane(
+      (unsigned)(unsigned long)(__attribute__((address_space(3))) const void *)lds_block);
+  unsigned saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds_addr), "v"(byte_off), "s"(r));
+}
+
 // Copies a ROWS x D bf16 tile (row-major at `src`, `valid` rows before the
 // end of the sequence) into a row-major, swizzled LDS tile, NW waves sharing
 // the work: copy jj of wave w fills LDS bytes [(w*NDMA + jj) * 1024, +1024);
 // lane l writes element e = blk*512 + 8l, i.e. row e / D and physical 16-byte
 // block (e % D) / 8, which holds logical block (physical ^ swz_f(row)) of the
 // row.  Rows at or past `valid` read as zeros.
+// Byte-addressed dma16_async (non-bf16 LDS data such as fp32 row terms).
+__device__ __forceinline__ void dma16b_async(u32x4 r, const void *lds_block, int byte_off) {
+  dma16_async(r, (const bf16 *)lds_block, byte_off);
+}
+
 template <int D, int ROWS, int NW>
 struct TileCopier {
   static constexpr int NDMA = ROWS * D * 2 / 1024 / NW;  // copies per wave
@@ -160,6 +202,9 @@ struct TileCopier {
 #pragma unroll
     for (int jj = 0; jj < NDMA; ++jj) dma16(r, dst + (wave * NDMA + jj) * 512, off[jj]);
   }
+  // the same copy issued with dma16_async (the caller waits with wait_vmem)
+  __device__ __forceinline__ void copy_async(bf16 *dst, const bf16 *src, int valid,
+                                             int wave) const;
 };
 
 // A operand (32 x 16) of a product contracting over the rows of a row-major
@@ -186,6 +231,14 @@ __device__ __forceinline__ void TileCopier<D, ROWS, NW>::init(int wave, int lane
     const int row = e / D, pblk = (e % D) / 8;
     off[jj] = row * D * 2 + 16 * (pblk ^ swz_f<D>(row));
   }
+}
+
+template <int D, int ROWS, int NW>
+__device__ __forceinline__ void TileCopier<D, ROWS, NW>::copy_async(bf16 *dst, const bf16 *src,
+                                                                    int valid, int wave) const {
+  const u32x4 r = rsrc_words(src, valid * D * 2);
+#pragma unroll
+  for (int jj = 0; jj < NDMA; ++jj) dma16_async(r, dst + (wave * NDMA + jj) * 512, off[jj]);
 }
 
 // s_waitcnt vmcnt(n) for a compile-time n < 16
