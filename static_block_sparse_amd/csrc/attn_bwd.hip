@@ -142,19 +142,19 @@ __global__ __launch_bounds__(T / 32 * 64, 1) void radial_bwd_dkdv_kernel(
   cp.init(wave, lane);
   // copies of chunk c (first row m0) into buffer c % NB; issued from inline
   // assembly (see dma16_async), so every wait below is explicit
-  auto issue = [&](int c, int m0) {
+  // (half 0: Q and the LSE terms; half 1: dO and the Delta terms)
+  auto issue_half = [&](int c, int m0, int half) {
     const int buf = c % NB;
-    bf16 *qd = lds_t + buf * 2 * C::CHUNK;
-    cp.copy_async(qd, Qb + (int64_t)m0 * D, N - m0, wave);
-    cp.copy_async(qd + C::CHUNK, dOb + (int64_t)m0 * D, N - m0, wave);
+    bf16 *qd = lds_t + buf * 2 * C::CHUNK + half * C::CHUNK;
+    cp.copy_async(qd, (half ? dOb : Qb) + (int64_t)m0 * D, N - m0, wave);
     // row terms: wave w copies floats [w * 4 LPW, (w + 1) * 4 LPW) of each
-    float *rd = lds_r + buf * 2 * C::MC + wave * 4 * C::LPW;
-    const u32x4 rl = rsrc_words(LSE + rbase + m0, (N - m0) * 4);
-    const u32x4 rdl = rsrc_words(Delta + rbase + m0, (N - m0) * 4);
-    if (lane < C::LPW) {
-      dma16b_async(rl, rd, (wave * 4 * C::LPW + 4 * lane) * 4);
-      dma16b_async(rdl, rd + C::MC, (wave * 4 * C::LPW + 4 * lane) * 4);
-    }
+    float *rd = lds_r + buf * 2 * C::MC + half * C::MC + wave * 4 * C::LPW;
+    const u32x4 rl = rsrc_words((half ? Delta : LSE) + rbase + m0, (N - m0) * 4);
+    if (lane < C::LPW) dma16b_async(rl, rd, (wave * 4 * C::LPW + 4 * lane) * 4);
+  };
+  auto issue = [&](int c, int m0) {
+    issue_half(c, m0, 0);
+    issue_half(c, m0, 1);
   };
 
   // stage-1 results of a block: sd[0] = S, sd[1] = dP (register r holds
@@ -289,9 +289,15 @@ __global__ __launch_bounds__(T / 32 * 64, 1) void radial_bwd_dkdv_kernel(
     chunk_end(0);
     // chunk iterations 1 .. nch - 1: steps 2c, 2c + 1
     for (int c = 1; c < nch; ++c) {
-      if (c + 2 < nch) issue(c + 2, row_d);
+      // the copies of chunk c + 2 go out in two halves, one per step: a
+      // single burst from every wave queues at the CU's address unit and
+      // stalls instruction issue
+      const bool more = c + 2 < nch;
+      const int row_e = row_d;
+      if (more) issue_half(c + 2, row_e, 0);
       row_d = c + 3 < nch ? row0_of(c + 3) : 0;
       step(2 * c, YES, YES, YES, sdA, sdB, pdB, pdA);
+      if (more) issue_half(c + 2, row_e, 1);
       step(2 * c + 1, YES, YES, YES, sdB, sdA, pdA, pdB);
       chunk_end(c);
     }
