@@ -7,11 +7,11 @@ oracle can draw identical inputs from it without sharing any method code.
 The shapes stand in for the video models the radial-attention pages evaluate
 (HunyuanVideo 5 s 720p, Wan2.1-14B 720p, 4x-longer HunyuanVideo, and a
 training step); their latent videos are not available, so Q, K, V (and dO)
-are i.i.d. N(0, 1) draws rounded to bf16 (for the HunyuanVideo 5 s shape,
-Q, K and V are scaled by 1/sqrt(D) before rounding).  The work the kernels do
-depends only on the shapes and the mask; their speed does depend on the
-values a little, because the clock the GPU sustains depends on the power the
-arithmetic draws.
+are i.i.d. N(0, 1) draws rounded to bf16 (the 1/sqrt(D) that one workload
+description mentions is the softmax scale, applied by the kernels).  The work
+the kernels do depends only on the shapes and the mask; their speed does
+depend on the values, because the clock the GPU sustains depends on the power
+the arithmetic draws.
 """
 
 from __future__ import annotations
@@ -51,8 +51,7 @@ WORKLOADS = {
         Workload("tiny_f8_s256", 1, 2, 8, 256, 64, 64, 1,
                  desc="tiny radial attention fwd: 8 frames x 256 tokens, D=64, 64x64 tiles"),
         Workload("hunyuan_5s_720p", 1, 24, 33, 3600, 128, 128, 2,
-                 desc="HunyuanVideo-shaped 5 s 720p fwd: 33 latent frames x 3600 tokens (80x45)",
-                 input_scale=1.0 / math.sqrt(128)),
+                 desc="HunyuanVideo-shaped 5 s 720p fwd: 33 latent frames x 3600 tokens (80x45)"),
         Workload("wan21_720p", 1, 40, 21, 3600, 128, 128, 3,
                  desc="Wan2.1-14B-shaped 720p fwd: 21 latent frames x 3600 tokens"),
         Workload("hunyuan_4x_long", 1, 24, 129, 3600, 128, 128, 4,
