@@ -70,6 +70,22 @@ __global__ __launch_bounds__(256) void radial_bwd_pre_kernel(const bf16 *__restr
 //    Step pairs form a chunk iteration c, which reads chunks c and c - 1 while
 //    the copies of chunk c + 2 are in flight.
 // ---------------------------------------------------------------------------
+// v_mfma_f32_32x32x16_bf16 with its result and accumulator in vector
+// registers and B in accumulation registers, written out so that one kernel
+// can mix this form with the compiler's accumulation-register form (the
+// compiler picks one form per function).  Callers keep its hazards: the
+// result is read by vector instructions only several products later, and a
+// chain of these on one accumulator alternates with another chain.
+__device__ __forceinline__ f32x16 mfma_v(bf16x8 a, bf16x8 b, f32x16 c) {
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "a"(b));
+  return c;
+}
+__device__ __forceinline__ f32x16 mfma_v0(bf16x8 a, bf16x8 b) {
+  f32x16 d;
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(b));
+  return d;
+}
+
 template <int D, int T>
 struct DkdvCfg {
   static constexpr int NW = T / 32;
@@ -101,7 +117,11 @@ __global__ __launch_bounds__(T / 32 * 64, 1) void radial_bwd_dkdv_kernel(
     float scale_log2, float scale) {
   using C = DkdvCfg<D, T>;
   constexpr int NB = C::NBUF;
-  __shared__ __attribute__((aligned(1024))) bf16 lds_t[NB * 2 * C::CHUNK];
+  // Q and dO chunk buffers in two arrays of NB * CHUNK elements (64 KB each
+  // at D = 128), so every LDS read is a per-lane register plus an immediate
+  // offset (below 64 KB) whatever the buffer
+  __shared__ __attribute__((aligned(1024))) bf16 lds_q[NB * C::CHUNK];
+  __shared__ __attribute__((aligned(1024))) bf16 lds_do[NB * C::CHUNK];
   __shared__ __attribute__((aligned(16))) float lds_r[NB * 2 * C::MC];
 
   const int tid = threadIdx.x;
@@ -122,6 +142,9 @@ __global__ __launch_bounds__(T / 32 * 64, 1) void radial_bwd_dkdv_kernel(
   for (int kk = 0; kk < C::NKK; ++kk) {
     kf[kk] = k_ok ? ld8(K + base + (int64_t)key * D + kk * 16 + g * 8) : zero_bf16x8();
     vf[kk] = k_ok ? ld8(V + base + (int64_t)key * D + kk * 16 + g * 8) : zero_bf16x8();
+    // K and V are only ever MFMA operands: keep them in accumulation
+    // registers, leaving the vector registers to the pipeline stages
+    asm volatile("" : "+a"(kf[kk]), "+a"(vf[kk]));
   }
   f32x16 adk[C::NDB], adv[C::NDB];
 #pragma unroll
@@ -136,115 +159,123 @@ __global__ __launch_bounds__(T / 32 * 64, 1) void radial_bwd_dkdv_kernel(
   int nch = (t_end - t_begin) * C::CPT;
   if (t_end > t_begin && row_idx[t_end - 1] == nb - 1)
     nch -= C::CPT - (N - (nb - 1) * T + C::MC - 1) / C::MC;
-  auto row0_of = [&](int c) { return row_idx[t_begin + c / C::CPT] * T + (c % C::CPT) * C::MC; };
+  auto row0_of = [&](int c) __attribute__((always_inline)) { return row_idx[t_begin + c / C::CPT] * T + (c % C::CPT) * C::MC; };
 
   typename C::Copier cp;
   cp.init(wave, lane);
   // copies of chunk c (first row m0) into buffer c % NB; issued from inline
   // assembly (see dma16_async), so every wait below is explicit
   // (half 0: Q and the LSE terms; half 1: dO and the Delta terms)
-  auto issue_half = [&](int c, int m0, int half) {
+  auto issue_half = [&](int c, int m0, int half) __attribute__((always_inline)) {
     const int buf = c % NB;
-    bf16 *qd = lds_t + buf * 2 * C::CHUNK + half * C::CHUNK;
+    bf16 *qd = (half ? lds_do : lds_q) + buf * C::CHUNK;
     cp.copy_async(qd, (half ? dOb : Qb) + (int64_t)m0 * D, N - m0, wave);
     // row terms: wave w copies floats [w * 4 LPW, (w + 1) * 4 LPW) of each
     float *rd = lds_r + buf * 2 * C::MC + half * C::MC + wave * 4 * C::LPW;
     const u32x4 rl = rsrc_words((half ? Delta : LSE) + rbase + m0, (N - m0) * 4);
     if (lane < C::LPW) dma16b_async(rl, rd, (wave * 4 * C::LPW + 4 * lane) * 4);
   };
-  auto issue = [&](int c, int m0) {
+  auto issue = [&](int c, int m0) __attribute__((always_inline)) {
     issue_half(c, m0, 0);
     issue_half(c, m0, 1);
   };
 
   // stage-1 results of a block: sd[0] = S, sd[1] = dP (register r holds
-  // query row 32 (j % 2) + 8 (r / 4) + 4 g + r % 4 of the chunk, for key
-  // column c32), and the LSE (rt[0..3]) and Delta (rt[4..7]) of those rows
+  // query row 32 mb + 8 (r / 4) + 4 g + r % 4 of the chunk, for key column
+  // c32)
   struct Blk {
     f32x16 sd[2];
-    f32x4 rt[8];
-  };
-  // stage 1 of block j
-  auto stage1 = [&](int j, Blk &b) {
-    const int buf = (j >> 1) % NB, mb = j & 1;
-    const bf16 *Qs = lds_t + buf * 2 * C::CHUNK;
-    const bf16 *dOs = Qs + C::CHUNK;
-#pragma unroll
-    for (int kk = 0; kk < C::NKK; ++kk) {
-      const bf16x8 qa = ld8(Qs + swz<D>(mb * 32 + c32, 2 * kk + g));
-      const bf16x8 da = ld8(dOs + swz<D>(mb * 32 + c32, 2 * kk + g));
-      b.sd[0] = mfma32(qa, kf[kk], kk == 0 ? zero16() : b.sd[0]);
-      b.sd[1] = mfma32(da, vf[kk], kk == 0 ? zero16() : b.sd[1]);
-    }
-    const float *lse_s = lds_r + buf * 2 * C::MC + 32 * mb;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      b.rt[i] = *reinterpret_cast<const f32x4 *>(&lse_s[8 * i + 4 * g]);
-      b.rt[4 + i] = *reinterpret_cast<const f32x4 *>(&lse_s[C::MC + 8 * i + 4 * g]);
-    }
-  };
-  // stage 2 of block j: pd[0] = P, pd[1] = dS, rounded to bf16
-  auto stage2 = [&](const Blk &b, bf16x8 (&pd)[2][2]) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int r = 4 * i + jj;
-        const float p = fast_exp2(fmaf(b.sd[0][r], scale_log2, -b.rt[i][jj] * kLog2e));
-        pd[0][r >> 3][r & 7] = bf16(p);
-        pd[1][r >> 3][r & 7] = bf16(p * (b.sd[1][r] - b.rt[4 + i][jj]));
-      }
-    }
-  };
-  // stage 3 of block j: dV^T += dO^T P, dK^T += Q^T dS
-  auto stage3 = [&](int j, const bf16x8 (&pd)[2][2]) {
-    const bf16 *Qs = lds_t + ((j >> 1) % NB) * 2 * C::CHUNK;
-    const bf16 *dOs = Qs + C::CHUNK;
-    const int mb = j & 1;
-#pragma unroll
-    for (int db = 0; db < C::NDB; ++db) {
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        adv[db] = mfma32(ld_trA<D>(dOs, db, mb, ks, lane), pd[0][ks], adv[db]);
-        adk[db] = mfma32(ld_trA<D>(Qs, db, mb, ks, lane), pd[1][ks], adk[db]);
-      }
-    }
   };
 
-  // step j: stage 3 of j - 2, stage 2 of j - 1, stage 1 of j (as flagged)
-  auto step = [&](int j, auto F1, auto F2, auto F3, Blk &sd_new, const Blk &sd_old,
-                  bf16x8 (&pd_new)[2][2], const bf16x8 (&pd_old)[2][2]) {
+  // Step j: stage 3 of block j - 2 (chunk buffer b3, half m3), stage 2 of
+  // block j - 1 (b2, m2), stage 1 of block j (b1, m1), as flagged.  The step
+  // is written as an explicit schedule of product slots (stage 3's products,
+  // then stage 1's): slot i issues the LDS reads of slot i + RA, its own
+  // product and, from slot 4 on, a share of stage 2's elements (whose LSE and
+  // Delta terms are read in slots 0..3); a scheduling barrier after each slot
+  // keeps that order.  With one wave per SIMD, LDS latency is hidden only by
+  // this read-ahead and the vector work only by this interleaving.
+  auto step = [&](auto F1, auto F2, auto F3, int b1, int m1, int b2, int m2, int b3, int m3,
+                  Blk &sd_new, const Blk &sd_old, bf16x8 (&pd_new)[2][2],
+                  const bf16x8 (&pd_old)[2][2]) __attribute__((always_inline)) {
     constexpr bool s1 = decltype(F1)::value, s2 = decltype(F2)::value,
                    s3 = decltype(F3)::value;
-    constexpr int NM = 4 * C::NDB;  // products per stage
-    if constexpr (s3) stage3(j - 2, pd_old);
-    if constexpr (s2) stage2(sd_old, pd_new);
-    if constexpr (s1) stage1(j, sd_new);
-    // per product: its operand reads run ahead and a few vector-ALU
-    // instructions of stage 2 go along
-    // (0x008 products, 0x100 LDS reads, 0x002 vector ALU, 0x400 exp2)
-    if constexpr (s3) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+    constexpr int NM = 4 * C::NDB;                      // products per stage
+    constexpr int N3 = s3 ? NM : 0, NSL = N3 + (s1 ? NM : 0);
+    constexpr int RA = 4;                               // read-ahead (slots)
+    const bf16 *Qs3 = lds_q + b3 * C::CHUNK, *dOs3 = lds_do + b3 * C::CHUNK;
+    const bf16 *Qs1 = lds_q + b1 * C::CHUNK, *dOs1 = lds_do + b1 * C::CHUNK;
+    const float *rt2 = lds_r + b2 * 2 * C::MC + 32 * m2;
+    // operand of slot i: stage 3 slot -> (db, ks, dV or dK), stage 1 slot ->
+    // (kk, S or dP)
+    auto frag = [&](int i) __attribute__((always_inline)) {
+      if (i < N3) {
+        const int db = i / 4, ks = (i / 2) % 2;
+        return ld_trA<D>(i % 2 ? Qs3 : dOs3, db, m3, ks, lane);
+      }
+      const int kk = (i - N3) / 2;
+      return ld8((((i - N3) % 2) ? dOs1 : Qs1) + swz<D>(m1 * 32 + c32, 2 * kk + g));
+    };
+    auto product = [&](int i, bf16x8 a) __attribute__((always_inline)) {
+      if (i < N3) {
+        const int db = i / 4, ks = (i / 2) % 2;
+        if (i % 2 == 0)
+          adv[db] = mfma32(a, pd_old[0][ks], adv[db]);
+        else
+          adk[db] = mfma32(a, pd_old[1][ks], adk[db]);
+      } else {
+        const int kk = (i - N3) / 2, w = (i - N3) % 2;
+        sd_new.sd[w] = kk == 0 ? mfma_v0(a, w ? vf[kk] : kf[kk])
+                               : mfma_v(a, w ? vf[kk] : kf[kk], sd_new.sd[w]);
+      }
+    };
+    f32x4 rt[8];  // stage 2's LSE (0..3) and Delta (4..7) terms
+    auto rt_read = [&](int q) __attribute__((always_inline)) {
+      rt[q] = *reinterpret_cast<const f32x4 *>(&rt2[(q < 4 ? 0 : C::MC) + 8 * (q % 4) + 4 * g]);
+    };
+    // stage 2, element pair e (rows r = 2e, 2e + 1 of the block)
+    auto stage2_pair = [&](int e) __attribute__((always_inline)) {
 #pragma unroll
-      for (int i = 0; i < NM; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-        if constexpr (s2) {
-          __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
-          if (i % 2 == 0) __builtin_amdgcn_sched_group_barrier(0x400, 1, 0);
+      for (int t = 0; t < 2; ++t) {
+        const int r = 2 * e + t, i = r / 4, jj = r % 4;
+        const float p = fast_exp2(fmaf(sd_old.sd[0][r], scale_log2, -rt[i][jj] * kLog2e));
+        pd_new[0][r >> 3][r & 7] = bf16(p);
+        pd_new[1][r >> 3][r & 7] = bf16(p * (sd_old.sd[1][r] - rt[4 + i][jj]));
+      }
+    };
+    // stage 2 runs alongside stage 3's products when there are any (so the
+    // old S, dP die before stage 1 produces the new ones), else stage 1's
+    constexpr int S0 = 4;                                  // first stage-2 slot
+    constexpr int SEND = N3 > 0 ? N3 : NSL;                // slots [S0, SEND) carry it
+    constexpr int SPAN = SEND > S0 ? SEND - S0 : 1;
+    bf16x8 fr[NSL > 0 ? NSL : 1];
+#pragma unroll
+    for (int i = 0; i < RA && i < NSL; ++i) fr[i] = frag(i);
+#pragma unroll
+    for (int i = 0; i < NSL; ++i) {
+      if constexpr (s2) {
+        if (i < 2) {
+#pragma unroll
+          for (int q = 4 * i; q < 4 * i + 4; ++q) rt_read(q);
         }
       }
+      if (i + RA < NSL) fr[i + RA] = frag(i + RA);
+      product(i, fr[i]);
+      if constexpr (s2) {
+        // pairs [e0, e1) go with slot i
+        if (i >= S0 && i < SEND) {
+          const int e0 = (i - S0) * 8 / SPAN, e1 = (i - S0 + 1) * 8 / SPAN;
+#pragma unroll
+          for (int e = e0; e < e1; ++e) stage2_pair(e);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if constexpr (s1) {
+    if constexpr (s2 && SEND <= S0) {
 #pragma unroll
-      for (int i = 0; i < NM; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        if constexpr (s2) {
-          __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
-          if (i % 2 == 0) __builtin_amdgcn_sched_group_barrier(0x400, 1, 0);
-        }
-      }
+      for (int q = 0; q < 8; ++q) rt_read(q);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) stage2_pair(e);
     }
     // keeps stage 2 in this block (otherwise it may be sunk past the chunk
     // end's branches, away from the products it overlaps with)
@@ -272,7 +303,7 @@ __global__ __launch_bounds__(T / 32 * 64, 1) void radial_bwd_dkdv_kernel(
 
   // end of chunk iteration c: chunk c + 1 landed and visible (c + 2 may be
   // in flight); the buffer of chunk c - 1 is free afterwards
-  auto chunk_end = [&](int c) {
+  auto chunk_end = [&](int c) __attribute__((always_inline)) {
     if (c + 2 < nch)
       wait_vmem_n<C::NCOPY>();
     else
@@ -284,26 +315,27 @@ __global__ __launch_bounds__(T / 32 * 64, 1) void radial_bwd_dkdv_kernel(
     // chunk iteration 0: steps 0 and 1
     if (nch > 2) issue(2, row_c);
     int row_d = nch > 3 ? row0_of(3) : 0;
-    step(0, YES, NO, NO, sdA, sdB, pdB, pdA);
-    step(1, YES, YES, NO, sdB, sdA, pdA, pdB);
+    step(YES, NO, NO, 0, 0, 0, 0, 0, 0, sdA, sdB, pdB, pdA);
+    step(YES, YES, NO, 0, 1, 0, 0, 0, 0, sdB, sdA, pdA, pdB);
     chunk_end(0);
-    // chunk iterations 1 .. nch - 1: steps 2c, 2c + 1
+    // chunk iterations 1 .. nch - 1: steps 2c and 2c + 1; the copies of
+    // chunk c + 2 go out in two halves, one per step (a single burst from
+    // every wave queues at the CU's address unit and stalls instruction issue)
     for (int c = 1; c < nch; ++c) {
-      // the copies of chunk c + 2 go out in two halves, one per step: a
-      // single burst from every wave queues at the CU's address unit and
-      // stalls instruction issue
+      const int bc = c % NB, bp = (c + NB - 1) % NB;
       const bool more = c + 2 < nch;
       const int row_e = row_d;
       if (more) issue_half(c + 2, row_e, 0);
       row_d = c + 3 < nch ? row0_of(c + 3) : 0;
-      step(2 * c, YES, YES, YES, sdA, sdB, pdB, pdA);
+      step(YES, YES, YES, bc, 0, bp, 1, bp, 0, sdA, sdB, pdB, pdA);
       if (more) issue_half(c + 2, row_e, 1);
-      step(2 * c + 1, YES, YES, YES, sdB, sdA, pdA, pdB);
+      step(YES, YES, YES, bc, 1, bc, 0, bp, 1, sdB, sdA, pdA, pdB);
       chunk_end(c);
     }
-    // drain: steps 2 nch, 2 nch + 1
-    step(2 * nch, NO, YES, YES, sdA, sdB, pdB, pdA);
-    step(2 * nch + 1, NO, NO, YES, sdB, sdA, pdA, pdB);
+    // drain: steps 2 nch, 2 nch + 1 (chunk nch - 1)
+    const int bl = (nch - 1) % NB;
+    step(NO, YES, YES, 0, 0, bl, 1, bl, 0, sdA, sdB, pdB, pdA);
+    step(NO, NO, YES, 0, 0, 0, 0, bl, 1, sdB, sdA, pdA, pdB);
   }
 
   if (k_ok) {
