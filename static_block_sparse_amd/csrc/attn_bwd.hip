@@ -160,6 +160,10 @@ __global__ __launch_bounds__(T / 32 * 64, 1) void radial_bwd_dkdv_kernel(
   if (t_end > t_begin && row_idx[t_end - 1] == nb - 1)
     nch -= C::CPT - (N - (nb - 1) * T + C::MC - 1) / C::MC;
   auto row0_of = [&](int c) __attribute__((always_inline)) { return row_idx[t_begin + c / C::CPT] * T + (c % C::CPT) * C::MC; };
+  // the query tile of chunk c (clamped to the column), a raw scalar load
+  auto tile_of = [&](int c) __attribute__((always_inline)) {
+    return row_idx[t_begin + (c < nch ? c : nch - 1) / C::CPT];
+  };
 
   typename C::Copier cp;
   cp.init(wave, lane);
@@ -314,9 +318,13 @@ __global__ __launch_bounds__(T / 32 * 64, 1) void radial_bwd_dkdv_kernel(
   if (nch > 0) {
     // chunk iteration 0: steps 0 and 1
     if (nch > 2) issue(2, row_c);
-    int row_d = nch > 3 ? row0_of(3) : 0;
     step(YES, NO, NO, 0, 0, 0, 0, 0, 0, sdA, sdB, pdB, pdA);
     step(YES, YES, NO, 0, 1, 0, 0, 0, 0, sdB, sdA, pdA, pdB);
+    // The query tile of the chunk after next is loaded here, after the
+    // step's last LDS read and unused until the next iteration: scalar loads
+    // return out of order with LDS reads, so while one is in flight every
+    // LDS wait would have to drain everything.
+    int tile_d = tile_of(3);
     chunk_end(0);
     // chunk iterations 1 .. nch - 1: steps 2c and 2c + 1; the copies of
     // chunk c + 2 go out in two halves, one per step (a single burst from
@@ -324,12 +332,12 @@ __global__ __launch_bounds__(T / 32 * 64, 1) void radial_bwd_dkdv_kernel(
     for (int c = 1; c < nch; ++c) {
       const int bc = c % NB, bp = (c + NB - 1) % NB;
       const bool more = c + 2 < nch;
-      const int row_e = row_d;
+      const int row_e = tile_d * T + ((c + 2) % C::CPT) * C::MC;
       if (more) issue_half(c + 2, row_e, 0);
-      row_d = c + 3 < nch ? row0_of(c + 3) : 0;
       step(YES, YES, YES, bc, 0, bp, 1, bp, 0, sdA, sdB, pdB, pdA);
       if (more) issue_half(c + 2, row_e, 1);
       step(YES, YES, YES, bc, 1, bc, 0, bp, 1, sdB, sdA, pdA, pdB);
+      tile_d = tile_of(c + 3);
       chunk_end(c);
     }
     // drain: steps 2 nch, 2 nch + 1 (chunk nch - 1)
