@@ -235,3 +235,89 @@ def effective_mask(f: int, s: int, T: int, sink: bool = True,
     kept = kept_tiles_bruteforce(tok, T)
     t = np.arange(n) // T
     return kept[t[:, None], t[None, :]]
+
+
+# ----------------------------------------------------------------------------
+# Token-exact semantics: full and partial tiles (paper Eq.4 at token
+# granularity; review Step 3, "4-D mask" flattened).  Under token-exact
+# semantics a kept tile is computed with the token predicate applied inside
+# it; a tile in which every valid token pair is allowed needs no masking.
+# ----------------------------------------------------------------------------
+
+def full_tiles(f: int, s: int, T: int, sink: bool = True) -> np.ndarray:
+    """Boolean [nb, nb] tile map: full[u, v] iff tile (u, v) is kept and every
+    token pair (q, k) in it with q, k < n is allowed.
+
+    For a query q = (i, a) the allowed keys of frame j form one contiguous run
+    of positions b (see ``kept_tiles``), possibly empty.  The keys of frame j
+    that every query of tile u may attend are the intersection of those runs.
+    Tile v is full iff, for every frame j its keys fall in, those keys lie
+    inside the intersection for frame j.
+    """
+    n = f * s
+    nb = n_blocks(n, T)
+    tab = band_table(f, s)
+    kept = kept_tiles(f, s, T, sink)
+    full = np.zeros_like(kept)
+    q = np.arange(n, dtype=np.int64)
+    qi, qa = np.divmod(q, s)
+    for u in range(nb):
+        rows = slice(u * T, min(n, (u + 1) * T))
+        i, a = qi[rows], qa[rows]
+        common_lo = np.zeros(f, dtype=np.int64)
+        common_hi = np.full(f, -1, dtype=np.int64)      # empty by default
+        for j in range(f):
+            delta = np.abs(i - j)
+            w = tab[delta, 1]
+            period = tab[delta, 2]
+            lo = np.where(w >= 1, np.maximum(a - w + 1, 0), a)
+            hi = np.where(w >= 1, np.minimum(a + w - 1, s - 1), a)
+            has = (w >= 1) | (delta % period == 0)
+            if sink and j == 0:
+                lo = np.zeros_like(a)
+                hi = np.full_like(a, s - 1)
+                has = np.ones_like(has)
+            if has.all():
+                common_lo[j] = lo.max()
+                common_hi[j] = hi.min()
+        for v in np.nonzero(kept[u])[0]:
+            k0, k1 = v * T, min(n, (v + 1) * T) - 1
+            ok = True
+            for j in range(k0 // s, k1 // s + 1):
+                b0 = max(k0, j * s) - j * s
+                b1 = min(k1, (j + 1) * s - 1) - j * s
+                if not (common_lo[j] <= b0 and b1 <= common_hi[j]):
+                    ok = False
+                    break
+            full[u, v] = ok
+    return full
+
+
+def full_tiles_bruteforce(mask: np.ndarray, T: int) -> np.ndarray:
+    """AND-reduce a token mask [n, n] over T x T tiles, counting only the
+    valid pairs of ragged tiles, restricted to kept tiles."""
+    n = mask.shape[0]
+    nb = n_blocks(n, T)
+    pad = nb * T - n
+    m = np.pad(mask, ((0, pad), (0, pad)), constant_values=True)
+    allowed_all = m.reshape(nb, T, nb, T).all(axis=(1, 3))
+    return allowed_all & kept_tiles_bruteforce(mask, T)
+
+
+def token_mask_rows(f: int, s: int, rows: np.ndarray, sink: bool = True) -> np.ndarray:
+    """Boolean [len(rows), n]: the token predicate for the given query rows
+    against every key (the same predicate as ``allowed``, vectorised)."""
+    n = f * s
+    rows = np.asarray(rows, dtype=np.int64)
+    keys = np.arange(n, dtype=np.int64)
+    i, a = np.divmod(rows, s)
+    j, b = np.divmod(keys, s)
+    delta = np.abs(i[:, None] - j[None, :])
+    tab = band_table(f, s)
+    w = tab[delta, 1]
+    period = tab[delta, 2]
+    sep = np.abs(a[:, None] - b[None, :])
+    m = np.where(w >= 1, sep < w, (sep == 0) & (delta % period == 0))
+    if sink:
+        m = m | (j[None, :] == 0)
+    return m

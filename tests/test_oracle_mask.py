@@ -193,3 +193,47 @@ def test_tile_pairs_counts_valid_tokens():
     kept = om.kept_tiles(f, s, T, True)
     eff = om.effective_mask(f, s, T, True)
     assert om.tile_pairs(kept, f * s, T) == int(eff.sum())
+
+
+# ---- token-exact semantics: full and partial tiles ----------------------------
+
+@pytest.mark.parametrize("sink", [False, True])
+def test_full_tiles_match_bruteforce(sink):
+    # interval intersection vs AND-reduction of the brute-force token mask,
+    # over shapes with ragged tiles, tiles spanning several frames and the
+    # below-unit-width branch (s small, far frames)
+    for f, s, T in [(4, 9, 4), (8, 16, 8), (8, 16, 64), (5, 7, 3), (33, 3, 16),
+                    (12, 1, 4), (6, 100, 64), (3, 50, 128), (40, 2, 7), (20, 33, 32),
+                    (20, 5, 7), (9, 37, 16)]:
+        tok = om.token_mask(f, s, sink)
+        a = om.full_tiles(f, s, T, sink)
+        b = om.full_tiles_bruteforce(tok, T)
+        assert np.array_equal(a, b), (f, s, T, sink)
+        assert not (a & ~om.kept_tiles(f, s, T, sink)).any()  # full implies kept
+
+
+def test_full_tiles_dense_limit():
+    # f <= 2 allows every pair, so every kept (= every) tile is full
+    for f, s, T in [(1, 50, 16), (2, 37, 16), (2, 100, 64)]:
+        full = om.full_tiles(f, s, T, sink=False)
+        assert full.all()
+
+
+def test_full_tiles_pair_counts():
+    # pairs of full tiles are all allowed and the kept tiles hold every
+    # allowed pair: full pairs <= allowed pairs (closed form) <= kept pairs
+    f, s, T = 12, 40, 16
+    n = f * s
+    full = om.full_tiles(f, s, T, True)
+    kept = om.kept_tiles(f, s, T, True)
+    allowed = om.closed_form_pairs(f, s, True)
+    assert om.tile_pairs(full, n, T) <= allowed <= om.tile_pairs(kept, n, T)
+    assert 0 < full.sum() < kept.sum()
+
+
+def test_token_mask_rows_matches_token_mask():
+    f, s = 9, 16
+    tok = om.token_mask(f, s, True)
+    rows = np.array([0, 5, 16, 77, 143])
+    assert np.array_equal(om.token_mask_rows(f, s, rows, True), tok[rows])
+    assert np.array_equal(om.token_mask_rows(f, s, rows, False), om.token_mask(f, s, False)[rows])
