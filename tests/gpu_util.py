@@ -14,6 +14,13 @@ Tolerances (forward, bf16 inputs, fp32 accumulation):
       5 * 2^-9 * rms(O) ~ 0.01 rms(O) and mean |dO| by about 2^-10 rms(O).
       The guards take 5x margin: max |dO| <= 5e-2 rms(O_ref) and
       mean |dO| <= 1e-2 rms(O_ref).
+* Large elements: rounding is relative to each element's own size.  The
+  bf16 output is off by up to 2^-9 |x|, and an element made of a few
+  dominant terms keeps their bf16 rounding (P, dS: 2^-9 each) instead of
+  averaging it away, another ~2^-9 |x|.  Elements far above the rms (keys
+  of the sink frame, attended by every query, reach |dK| ~ 15 rms) then
+  exceed a bound in rms alone, so each element may also be off by
+  ELEM_REL * |ref| = 4 * 2^-9 * |ref| (2x margin over those two terms).
 * LSE: fp32 log-sum-exp of fp32 logits: max |dLSE| <= 1e-3.
 * Gradients: dQ, dK, dV are rounded to bf16 and built from bf16-rounded P
   and dS, the same error structure as O, so the same relative guards apply
@@ -38,6 +45,7 @@ O_MAX_ABS = 2e-2
 O_MEAN_ABS = 2e-3
 REL_MAX = 5e-2
 REL_MEAN = 1e-2
+ELEM_REL = 4 * 2.0 ** -9
 LSE_MAX_ABS = 1e-3
 PEAKY_REL_MAX = 1e-1
 
@@ -59,7 +67,9 @@ def check_close(got: np.ndarray, ref: np.ndarray, what: str, absolute: bool = Tr
         assert stats["max_abs"] / norm <= O_MAX_ABS, (what, stats)
         assert stats["mean_abs"] / norm <= O_MEAN_ABS, (what, stats)
     if rms > 0:
-        assert stats["max_abs"] <= rel_max * rms, (what, stats)
+        excess = float((err - ELEM_REL * np.abs(ref)).max())
+        stats["max_excess"] = excess
+        assert excess <= rel_max * rms, (what, stats)
         assert stats["mean_abs"] <= rel_mean * rms, (what, stats)
     return stats
 
