@@ -22,7 +22,9 @@ head, divided by the measured step time.  Extra objects:
   cpu_baseline -- the CPU oracle (float64 numpy) on a bounded sample of the
                   same workload, scaled to the same unit;
   dense        -- the same kernel on an all-tiles layout (dense attention);
-  bwd          -- the backward pass (dQ, dK, dV) on the same workload.
+  bwd          -- the backward pass (dQ, dK, dV) on the same workload;
+  token_exact  -- forward and backward with token-exact masking inside the
+                  partly covered tiles (same kept tiles, same flop count).
 """
 
 from __future__ import annotations
@@ -146,7 +148,7 @@ def main():
     ap.add_argument("--workload", default="hunyuan_5s_720p")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the dense and backward legs")
-    ap.add_argument("--only", choices=["fwd", "bwd", "dense", "copy"],
+    ap.add_argument("--only", choices=["fwd", "bwd", "dense", "exact", "copy"],
                     help="run only one leg (for profiler runs); prints no JSON")
     args = ap.parse_args()
 
@@ -249,14 +251,16 @@ def main():
                                "frac": round(dflops / dms / 1e9 / PEAK_BF16_TFLOPS, 4)}
         del Ld
 
-    if args.only in (None, "bwd") and not args.no_extras:
+    bflops = 10 * w.D * L.nnz_pairs * BH
+    do = ws = None
+    if args.only in (None, "bwd", "exact") and not args.no_extras:
         g = torch.Generator(dev).manual_seed(w.seed + 1000)
         do = torch.randn(q.shape, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
-        fwd()
-        dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
         ws = torch.empty(sba.lib().radial_attn_bwd_workspace_bytes(L.handle, w.B, w.H, w.N, w.D),
                          dtype=torch.uint8, device=dev)
-        bflops = 10 * w.D * L.nnz_pairs * BH
+
+    if args.only in (None, "bwd") and not args.no_extras:
+        fwd()
 
         def bwd():
             sba.attn_bwd(q, k, v, o, lse, do, L, w.scale, workspace=ws)
@@ -270,6 +274,37 @@ def main():
                              "frac": round(bflops / bms / 1e9 / PEAK_BF16_TFLOPS, 4),
                              "fwd_plus_bwd_ms": round(bms + result["ms_per_step"], 3),
                              "alg_flops": bflops}
+
+    if args.only in (None, "exact") and not args.no_extras:
+        Lx = sba.Layout(w.frames, w.tokens_per_frame, w.T, sink=True, token_exact=True)
+        Lx.upload(dev)
+        n_full = int(Lx.tile_flags()[0].sum())
+
+        def xfwd():
+            sba.attn_fwd(q, k, v, Lx, w.scale, out=o, lse=lse)
+
+        def xbwd():
+            sba.attn_bwd(q, k, v, o, lse, do, Lx, w.scale, workspace=ws)
+
+        st = 2 if args.only is None else args.steps
+        total_ms, _ = time_launches(xfwd, st, 1)
+        xf = total_ms / st
+        xfwd()
+        total_ms, _ = time_launches(xbwd, st, 1)
+        xb = total_ms / st
+        log(f"token-exact: fwd {xf:.2f} ms, bwd {xb:.2f} ms "
+            f"({n_full} of {Lx.nnz_tiles} kept tiles full)")
+        if result is not None:
+            result["token_exact"] = {
+                "fwd_ms": round(xf, 3), "bwd_ms": round(xb, 3),
+                "fwd_tflops": round(fwd_flops / xf / 1e9, 2),
+                "bwd_tflops": round(bflops / xb / 1e9, 2),
+                "fwd_overhead_vs_tile_mode": round(xf / result["ms_per_step"] - 1, 4),
+                "full_tile_fraction": round(n_full / Lx.nnz_tiles, 4)}
+            if "bwd" in result:
+                result["token_exact"]["bwd_overhead_vs_tile_mode"] = round(
+                    xb / result["bwd"]["ms"] - 1, 4)
+        del Lx
 
     if result is None:
         return

@@ -57,7 +57,13 @@ enum {
   RADIAL_SINK = 1u << 0,
   /* Keep every tile: plain dense attention through the same kernels, the
      in-library dense baseline. */
-  RADIAL_DENSE = 1u << 1
+  RADIAL_DENSE = 1u << 1,
+  /* Token-exact semantics: inside kept tiles only the allowed token pairs
+     take part (the mask of paper Eq.4 at token granularity, review Step 3),
+     instead of every pair of a kept tile.  The tile lists are the same; the
+     kernels apply the token predicate inside the tiles the layout marks
+     partial.  No effect together with RADIAL_DENSE (every tile is full). */
+  RADIAL_TOKEN_EXACT = 1u << 2
 };
 
 typedef struct radial_layout radial_layout; /* opaque */
@@ -81,11 +87,12 @@ typedef struct radial_layout radial_layout; /* opaque */
  *               caption).
  * A tile (u, v) is kept iff at least one allowed token pair lies in it, and
  * kept tiles are computed in full (review Step 5, paper §4.2: block-wise
- * computation in 128 x 128 blocks).  The last tile row/column is partial
+ * computation in 128 x 128 blocks); with RADIAL_TOKEN_EXACT only the
+ * allowed pairs inside them take part.  The last tile row/column is partial
  * when block_size does not divide n.
  *
  * frames >= 1, tokens_per_frame >= 1, n < 2^31, 1 <= block_size <= 4096.
- * flags: RADIAL_SINK | RADIAL_DENSE.  On success *out owns a new layout
+ * flags: RADIAL_SINK | RADIAL_DENSE | RADIAL_TOKEN_EXACT.  On success *out owns a new layout
  * (free with radial_layout_destroy); on failure *out is set to NULL.
  */
 int radial_mask_build(int64_t frames, int64_t tokens_per_frame, int32_t block_size,
@@ -104,6 +111,13 @@ int radial_layout_info(const radial_layout *L, int64_t *n_tokens, int32_t *n_blo
    key tile.  Any pointer may be NULL (that array is skipped). */
 int radial_layout_export(const radial_layout *L, int32_t *row_ptr, int32_t *col_idx,
                          int32_t *col_ptr, int32_t *row_idx);
+
+/* Full/partial marks of the kept tiles: csr_full[t] (CSR order) and
+   csc_full[t] (CSC order) are 1 when every token pair of tile t with row and
+   column < n is allowed, else 0 (the tiles token-exact semantics must mask
+   inside).  Filled for every layout; with RADIAL_DENSE every tile is full.
+   Any pointer may be NULL. */
+int radial_layout_tile_flags(const radial_layout *L, uint8_t *csr_full, uint8_t *csc_full);
 
 /* Band table, one entry per frame distance delta in [0, frames):
    band[delta] = r, width[delta] = w, period[delta] = sampling period
@@ -127,6 +141,8 @@ void radial_layout_destroy(radial_layout *L);
 /*
  * radial_attn_fwd -- O = softmax(scale * Q K^T + M) V under the layout's
  * mask M (review Step 0, paper §3 Eq.1/Eq.2), for every batch b and head h.
+ * M is 0 on every pair of a kept tile and -inf elsewhere; with
+ * RADIAL_TOKEN_EXACT it is 0 exactly on the allowed token pairs.
  *
  *   q, k, v : bf16 [B, H, N, D] inputs.
  *   o       : bf16 [B, H, N, D] output (rounded to nearest even).

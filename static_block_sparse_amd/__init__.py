@@ -21,12 +21,13 @@ import os
 import numpy as np
 
 __all__ = ["Layout", "attn_fwd", "attn_bwd", "lib", "LIB_PATH", "SINK", "DENSE",
-           "RadialError"]
+           "TOKEN_EXACT", "RadialError"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libradial.so")
 
 SINK = 1
 DENSE = 2
+TOKEN_EXACT = 4
 
 _STATUS = {0: "RADIAL_OK", -1: "RADIAL_E_INVALID", -2: "RADIAL_E_UNSUPPORTED",
            -3: "RADIAL_E_SHAPE", -4: "RADIAL_E_NOMEM", -5: "RADIAL_E_HIP", -6: "RADIAL_E_STATE"}
@@ -48,6 +49,7 @@ def _declare(L):
         "radial_mask_build": (c.c_int, [i64, i64, i32, u32, P(vp)]),
         "radial_layout_info": (c.c_int, [vp, P(i64), P(i32), P(i64), P(i64)]),
         "radial_layout_export": (c.c_int, [vp, vp, vp, vp, vp]),
+        "radial_layout_tile_flags": (c.c_int, [vp, vp, vp]),
         "radial_layout_band_table": (c.c_int, [vp, vp, vp, vp]),
         "radial_layout_token_mask": (c.c_int, [vp, vp, i64]),
         "radial_layout_upload": (c.c_int, [vp]),
@@ -83,11 +85,15 @@ def _check(status: int):
 
 
 class Layout:
-    """Block-sparse layout of the radial mask (owns a ``radial_layout``)."""
+    """Block-sparse layout of the radial mask (owns a ``radial_layout``).
+
+    ``token_exact=False`` (the default) computes every kept tile in full;
+    ``token_exact=True`` masks the tiles the mask only partly covers token by
+    token, so the attention follows the token mask exactly."""
 
     def __init__(self, frames: int, tokens_per_frame: int, block_size: int = 128,
-                 sink: bool = True, dense: bool = False):
-        flags = (SINK if sink else 0) | (DENSE if dense else 0)
+                 sink: bool = True, dense: bool = False, token_exact: bool = False):
+        flags = (SINK if sink else 0) | (DENSE if dense else 0) | (TOKEN_EXACT if token_exact else 0)
         h = ctypes.c_void_p()
         _check(lib().radial_mask_build(frames, tokens_per_frame, block_size, flags, ctypes.byref(h)))
         self._h = h
@@ -96,6 +102,7 @@ class Layout:
         self.block_size = block_size
         self.sink = sink
         self.dense = dense
+        self.token_exact = token_exact
         n, nb, nz, pairs = ctypes.c_int64(), ctypes.c_int32(), ctypes.c_int64(), ctypes.c_int64()
         _check(lib().radial_layout_info(h, ctypes.byref(n), ctypes.byref(nb), ctypes.byref(nz),
                                         ctypes.byref(pairs)))
@@ -126,6 +133,14 @@ class Layout:
         ri = np.empty(self.nnz_tiles, dtype=np.int32)
         _check(lib().radial_layout_export(self._h, None, None, cp.ctypes.data, ri.ctypes.data))
         return cp, ri
+
+    def tile_flags(self):
+        """(csr_full, csc_full): 1 where a kept tile holds only allowed pairs,
+        in the order of ``csr()[1]`` and ``csc()[1]``."""
+        a = np.empty(self.nnz_tiles, dtype=np.uint8)
+        b = np.empty(self.nnz_tiles, dtype=np.uint8)
+        _check(lib().radial_layout_tile_flags(self._h, a.ctypes.data, b.ctypes.data))
+        return a.astype(bool), b.astype(bool)
 
     def band_table(self):
         r = np.empty(self.frames, dtype=np.int32)

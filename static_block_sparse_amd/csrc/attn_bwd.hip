@@ -107,14 +107,14 @@ struct BwdFlag {
   static constexpr int value = V;
 };
 
-template <int D, int T>
+template <int D, int T, bool EXACT>
 __global__ __launch_bounds__(T / 32 * 64, 1) void radial_bwd_dkdv_kernel(
     const bf16 *__restrict__ Q, const bf16 *__restrict__ K, const bf16 *__restrict__ V,
     const bf16 *__restrict__ dO, const float *__restrict__ LSE,
     const float *__restrict__ Delta, bf16 *__restrict__ dK, bf16 *__restrict__ dV,
     const int32_t *__restrict__ col_ptr, const int32_t *__restrict__ row_idx,
     const int32_t *__restrict__ col_order, int32_t N, int32_t nb, int32_t n_work,
-    float scale_log2, float scale) {
+    float scale_log2, float scale, MaskGeom mg) {
   using C = DkdvCfg<D, T>;
   constexpr int NB = C::NBUF;
   // Q and dO chunk buffers in two arrays of NB * CHUNK elements (64 KB each
@@ -123,6 +123,9 @@ __global__ __launch_bounds__(T / 32 * 64, 1) void radial_bwd_dkdv_kernel(
   __shared__ __attribute__((aligned(1024))) bf16 lds_q[NB * C::CHUNK];
   __shared__ __attribute__((aligned(1024))) bf16 lds_do[NB * C::CHUNK];
   __shared__ __attribute__((aligned(16))) float lds_r[NB * 2 * C::MC];
+  // per buffer: first query row of its chunk, bit 31 set when the chunk's
+  // tile is marked partial (token-exact layouts)
+  __shared__ int lds_meta[NB];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -137,6 +140,8 @@ __global__ __launch_bounds__(T / 32 * 64, 1) void radial_bwd_dkdv_kernel(
 
   const int key = v * T + wave * 32 + c32;
   const bool k_ok = key < N;
+  // this lane's key as (frame, position), for the token predicate
+  const int kj = key / mg.s, kpos = key - (key / mg.s) * mg.s;
   bf16x8 kf[C::NKK], vf[C::NKK];
 #pragma unroll
   for (int kk = 0; kk < C::NKK; ++kk) {
@@ -157,9 +162,15 @@ __global__ __launch_bounds__(T / 32 * 64, 1) void radial_bwd_dkdv_kernel(
   // the chunks of the last query tile at or past N
   const int t_begin = col_ptr[v], t_end = col_ptr[v + 1];
   int nch = (t_end - t_begin) * C::CPT;
-  if (t_end > t_begin && row_idx[t_end - 1] == nb - 1)
+  if (t_end > t_begin && (row_idx[t_end - 1] & 0x7fffffff) == nb - 1)
     nch -= C::CPT - (N - (nb - 1) * T + C::MC - 1) / C::MC;
-  auto row0_of = [&](int c) __attribute__((always_inline)) { return row_idx[t_begin + c / C::CPT] * T + (c % C::CPT) * C::MC; };
+  // first query row of chunk c with bit 31 set when its tile is partial
+  auto code_of = [&](int raw, int c) __attribute__((always_inline)) {
+    return ((raw & 0x7fffffff) * T + (c % C::CPT) * C::MC) | (raw & int(0x80000000));
+  };
+  auto row0_of = [&](int c) __attribute__((always_inline)) {
+    return code_of(row_idx[t_begin + c / C::CPT], c);
+  };
   // the query tile of chunk c (clamped to the column), a raw scalar load
   auto tile_of = [&](int c) __attribute__((always_inline)) {
     return row_idx[t_begin + (c < nch ? c : nch - 1) / C::CPT];
@@ -170,8 +181,10 @@ __global__ __launch_bounds__(T / 32 * 64, 1) void radial_bwd_dkdv_kernel(
   // copies of chunk c (first row m0) into buffer c % NB; issued from inline
   // assembly (see dma16_async), so every wait below is explicit
   // (half 0: Q and the LSE terms; half 1: dO and the Delta terms)
-  auto issue_half = [&](int c, int m0, int half) __attribute__((always_inline)) {
+  auto issue_half = [&](int c, int code, int half) __attribute__((always_inline)) {
     const int buf = c % NB;
+    const int m0 = code & 0x7fffffff;
+    if (EXACT && half == 0 && tid == 0) lds_meta[buf] = code;
     bf16 *qd = (half ? lds_do : lds_q) + buf * C::CHUNK;
     cp.copy_async(qd, (half ? dOb : Qb) + (int64_t)m0 * D, N - m0, wave);
     // row terms: wave w copies floats [w * 4 LPW, (w + 1) * 4 LPW) of each
@@ -201,7 +214,7 @@ __global__ __launch_bounds__(T / 32 * 64, 1) void radial_bwd_dkdv_kernel(
   // this read-ahead and the vector work only by this interleaving.
   auto step = [&](auto F1, auto F2, auto F3, int b1, int m1, int b2, int m2, int b3, int m3,
                   Blk &sd_new, const Blk &sd_old, bf16x8 (&pd_new)[2][2],
-                  const bf16x8 (&pd_old)[2][2]) __attribute__((always_inline)) {
+                  const bf16x8 (&pd_old)[2][2], unsigned okm) __attribute__((always_inline)) {
     constexpr bool s1 = decltype(F1)::value, s2 = decltype(F2)::value,
                    s3 = decltype(F3)::value;
     constexpr int NM = 4 * C::NDB;                      // products per stage
@@ -242,7 +255,10 @@ __global__ __launch_bounds__(T / 32 * 64, 1) void radial_bwd_dkdv_kernel(
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         const int r = 2 * e + t, i = r / 4, jj = r % 4;
-        const float p = fast_exp2(fmaf(sd_old.sd[0][r], scale_log2, -rt[i][jj] * kLog2e));
+        float sv = sd_old.sd[0][r];
+        // token-exact: okm holds the stage-2 block's allowed rows (bit r)
+        if constexpr (EXACT) sv = ((okm >> r) & 1u) ? sv : -INFINITY;
+        const float p = fast_exp2(fmaf(sv, scale_log2, -rt[i][jj] * kLog2e));
         pd_new[0][r >> 3][r & 7] = bf16(p);
         pd_new[1][r >> 3][r & 7] = bf16(p * (sd_old.sd[1][r] - rt[4 + i][jj]));
       }
@@ -292,6 +308,19 @@ __global__ __launch_bounds__(T / 32 * 64, 1) void radial_bwd_dkdv_kernel(
   bf16x8 pdA[2][2], pdB[2][2];      // stage-2 results of even / odd blocks
   const BwdFlag<0> NO;
   const BwdFlag<1> YES;
+  // token-exact: this lane's allowed rows of block (buffer b, half m), read
+  // between steps (outside their fixed schedule); all rows when the block's
+  // tile is full
+  auto s2_bits = [&](int b, int m) __attribute__((always_inline)) {
+    if constexpr (!EXACT) {
+      return ~0u;
+    } else {
+      const int meta = lds_meta[b];
+      if (meta >= 0) return ~0u;
+      return lane_query_bits(kj, kpos, (meta & 0x7fffffff) + 32 * m, g, mg.s, mg.frames,
+                             mg.sink != 0);
+    }
+  };
 
   int row_a = nch > 0 ? row0_of(0) : 0;  // first rows of chunks c + 1, c + 2
   int row_b = nch > 1 ? row0_of(1) : 0;
@@ -318,8 +347,8 @@ __global__ __launch_bounds__(T / 32 * 64, 1) void radial_bwd_dkdv_kernel(
   if (nch > 0) {
     // chunk iteration 0: steps 0 and 1
     if (nch > 2) issue(2, row_c);
-    step(YES, NO, NO, 0, 0, 0, 0, 0, 0, sdA, sdB, pdB, pdA);
-    step(YES, YES, NO, 0, 1, 0, 0, 0, 0, sdB, sdA, pdA, pdB);
+    step(YES, NO, NO, 0, 0, 0, 0, 0, 0, sdA, sdB, pdB, pdA, ~0u);
+    step(YES, YES, NO, 0, 1, 0, 0, 0, 0, sdB, sdA, pdA, pdB, s2_bits(0, 0));
     // The query tile of the chunk after next is loaded here, after the
     // step's last LDS read and unused until the next iteration: scalar loads
     // return out of order with LDS reads, so while one is in flight every
@@ -332,18 +361,18 @@ __global__ __launch_bounds__(T / 32 * 64, 1) void radial_bwd_dkdv_kernel(
     for (int c = 1; c < nch; ++c) {
       const int bc = c % NB, bp = (c + NB - 1) % NB;
       const bool more = c + 2 < nch;
-      const int row_e = tile_d * T + ((c + 2) % C::CPT) * C::MC;
+      const int row_e = code_of(tile_d, c + 2);
       if (more) issue_half(c + 2, row_e, 0);
-      step(YES, YES, YES, bc, 0, bp, 1, bp, 0, sdA, sdB, pdB, pdA);
+      step(YES, YES, YES, bc, 0, bp, 1, bp, 0, sdA, sdB, pdB, pdA, s2_bits(bp, 1));
       if (more) issue_half(c + 2, row_e, 1);
-      step(YES, YES, YES, bc, 1, bc, 0, bp, 1, sdB, sdA, pdA, pdB);
+      step(YES, YES, YES, bc, 1, bc, 0, bp, 1, sdB, sdA, pdA, pdB, s2_bits(bc, 0));
       tile_d = tile_of(c + 3);
       chunk_end(c);
     }
     // drain: steps 2 nch, 2 nch + 1 (chunk nch - 1)
     const int bl = (nch - 1) % NB;
-    step(NO, YES, YES, 0, 0, bl, 1, bl, 0, sdA, sdB, pdB, pdA);
-    step(NO, NO, YES, 0, 0, 0, 0, bl, 1, sdB, sdA, pdA, pdB);
+    step(NO, YES, YES, 0, 0, bl, 1, bl, 0, sdA, sdB, pdB, pdA, s2_bits(bl, 1));
+    step(NO, NO, YES, 0, 0, 0, 0, bl, 1, sdB, sdA, pdA, pdB, ~0u);
   }
 
   if (k_ok) {
@@ -386,13 +415,13 @@ struct DqCfg {
   using Copier = TileCopier<D, KC, NW>;
 };
 
-template <int D, int T>
+template <int D, int T, bool EXACT>
 __global__ __launch_bounds__(T / 32 * 64, 2) void radial_bwd_dq_kernel(
     const bf16 *__restrict__ Q, const bf16 *__restrict__ K, const bf16 *__restrict__ V,
     const bf16 *__restrict__ dO, const float *__restrict__ LSE,
     const float *__restrict__ Delta, bf16 *__restrict__ dQ,
     const int32_t *__restrict__ row_ptr, const int32_t *__restrict__ col_idx, int32_t N,
-    int32_t nb, int32_t n_work, float scale_log2, float scale) {
+    int32_t nb, int32_t n_work, float scale_log2, float scale, MaskGeom mg) {
   using C = DqCfg<D, T>;
   __shared__ __attribute__((aligned(1024))) bf16 lds[4 * C::CHUNK];  // K0 V0 K1 V1
 
@@ -424,9 +453,15 @@ __global__ __launch_bounds__(T / 32 * 64, 2) void radial_bwd_dq_kernel(
 
   const int t_begin = row_ptr[u], t_end = row_ptr[u + 1];
   int nch = (t_end - t_begin) * C::CPT;
-  if (t_end > t_begin && col_idx[t_end - 1] == nb - 1)
+  if (t_end > t_begin && (col_idx[t_end - 1] & 0x7fffffff) == nb - 1)
     nch -= C::CPT - (N - (nb - 1) * T + C::KC - 1) / C::KC;
-  auto key_of = [&](int c) { return col_idx[t_begin + c / C::CPT] * T + (c % C::CPT) * C::KC; };
+  // first key of chunk c, with bit 31 set when its tile is marked partial
+  auto key_of = [&](int c) {
+    const int raw = col_idx[t_begin + c / C::CPT];
+    return ((raw & 0x7fffffff) * T + (c % C::CPT) * C::KC) | (raw & int(0x80000000));
+  };
+  // this lane's query as (frame, position), for the token predicate
+  const int qi = qrow / mg.s, qa = qrow - (qrow / mg.s) * mg.s;
 
   typename C::Copier cp;
   cp.init(wave, lane);
@@ -438,13 +473,18 @@ __global__ __launch_bounds__(T / 32 * 64, 2) void radial_bwd_dq_kernel(
 
   int key_n = nch > 0 ? key_of(0) : 0;   // first keys of chunks c and c + 1
   int key_nn = nch > 1 ? key_of(1) : 0;
-  if (nch > 0) issue(0, key_n);
+  if (nch > 0) issue(0, key_n & 0x7fffffff);
   wait_vmem();  // Q, dO fragments, LSE, Delta and the first chunk
   __syncthreads();
 
   for (int c = 0; c < nch; ++c) {
-    if (c + 1 < nch) issue(c + 1, key_nn);  // lands during this chunk
+    const int key0 = key_n & 0x7fffffff;
+    const bool partial = EXACT && key_n < 0;
+    if (c + 1 < nch) issue(c + 1, key_nn & 0x7fffffff);  // lands during this chunk
     const int key_3 = c + 2 < nch ? key_of(c + 2) : 0;
+    // token-exact: this lane's allowed keys of the chunk
+    const unsigned ok =
+        partial ? lane_key_bits<C::NKB>(qi, qa, key0, g, mg.s, mg.frames, mg.sink != 0) : ~0u;
     const bf16 *Ks = lds + (c & 1) * 2 * C::CHUNK;
     const bf16 *Vs = Ks + C::CHUNK;
 
@@ -463,6 +503,11 @@ __global__ __launch_bounds__(T / 32 * 64, 2) void radial_bwd_dq_kernel(
         dp = mfma32(va[kk], dof[kk], dp);
       }
       // register r holds key kb*32 + 8*(r/4) + 4g + r%4 of the chunk
+      if (partial) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (!((ok >> (16 * kb + r)) & 1u)) s[r] = -INFINITY;
+      }
       bf16x8 dsb[2];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -498,7 +543,7 @@ __global__ __launch_bounds__(T / 32 * 64, 2) void radial_bwd_dq_kernel(
   }
 }
 
-template <int D, int T>
+template <int D, int T, bool EXACT>
 hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t stream) {
   const int64_t rows = (int64_t)a.BH * a.N;
   constexpr int RPB = 256 / (D / 8);
@@ -509,18 +554,23 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t stream) {
   if (e != hipSuccess) return e;
   const int64_t works = (int64_t)a.BH * a.nb;
   const float sl2 = a.scale * kLog2e;
-  hipLaunchKernelGGL((radial_bwd_dkdv_kernel<D, T>), dim3((unsigned)works),
+  hipLaunchKernelGGL((radial_bwd_dkdv_kernel<D, T, EXACT>), dim3((unsigned)works),
                      dim3(DkdvCfg<D, T>::NT), 0, stream, (const bf16 *)a.q, (const bf16 *)a.k,
                      (const bf16 *)a.v, (const bf16 *)a.dout, a.lse, a.delta, (bf16 *)a.dk,
                      (bf16 *)a.dv, a.col_ptr, a.row_idx, a.col_order, a.N, a.nb, (int32_t)works,
-                     sl2, a.scale);
+                     sl2, a.scale, a.mask);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((radial_bwd_dq_kernel<D, T>), dim3((unsigned)works), dim3(DqCfg<D, T>::NT),
-                     0, stream, (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.v,
-                     (const bf16 *)a.dout, a.lse, a.delta, (bf16 *)a.dq, a.row_ptr, a.col_idx,
-                     a.N, a.nb, (int32_t)works, sl2, a.scale);
+  hipLaunchKernelGGL((radial_bwd_dq_kernel<D, T, EXACT>), dim3((unsigned)works),
+                     dim3(DqCfg<D, T>::NT), 0, stream, (const bf16 *)a.q, (const bf16 *)a.k,
+                     (const bf16 *)a.v, (const bf16 *)a.dout, a.lse, a.delta, (bf16 *)a.dq,
+                     a.row_ptr, a.col_idx, a.N, a.nb, (int32_t)works, sl2, a.scale, a.mask);
   return hipGetLastError();
+}
+
+template <int D, int T>
+hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t stream) {
+  return a.mask.exact ? launch_bwd_t<D, T, true>(a, stream) : launch_bwd_t<D, T, false>(a, stream);
 }
 
 hipError_t launch_bwd(const BwdArgs &a, hipStream_t stream) {

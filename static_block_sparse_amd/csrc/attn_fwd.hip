@@ -28,6 +28,9 @@
 //  * the running max is only moved when a chunk's max exceeds it by more
 //    than 8 (log2 units); probabilities then stay below 2^8, exact in the
 //    final O / l and LSE, and the O rescale is skipped on most chunks.
+//  * token-exact layouts (EXACT): in the chunks of tiles marked partial,
+//    each lane masks the keys outside its query's allowed runs (one per key
+//    frame the chunk touches, however many) before the max.
 #include <hip/hip_runtime.h>
 
 #include "device_common.h"
@@ -54,12 +57,12 @@ struct FwdCfg {
   static_assert(NDMA >= 1 && CHUNK * 2 % (1024 * NW) == 0, "chunk must split evenly");
 };
 
-template <int D, int T>
+template <int D, int T, bool EXACT>
 __global__ __launch_bounds__(T / 32 * 64, 2) void radial_fwd_kernel(
     const bf16 *__restrict__ Q, const bf16 *__restrict__ K, const bf16 *__restrict__ V,
     bf16 *__restrict__ O, float *__restrict__ LSE, const int32_t *__restrict__ row_ptr,
     const int32_t *__restrict__ col_idx, int32_t N, int32_t nb, int32_t n_work,
-    float scale_log2) {
+    float scale_log2, MaskGeom mg) {
   using C = FwdCfg<D, T>;
   constexpr float kSlack = 8.f;  // lazy-rescale threshold (log2 units)
   __shared__ __attribute__((aligned(1024))) bf16 lds[2 * C::BUF];
@@ -85,13 +88,17 @@ __global__ __launch_bounds__(T / 32 * 64, 2) void radial_fwd_kernel(
   // the last key tile that lie entirely at or beyond N
   const int t_begin = row_ptr[u], t_end = row_ptr[u + 1];
   int nchunks = (t_end - t_begin) * C::CPT;
-  if (t_end > t_begin && col_idx[t_end - 1] == nb - 1)
+  if (t_end > t_begin && (col_idx[t_end - 1] & 0x7fffffff) == nb - 1)
     nchunks -= C::CPT - (N - (nb - 1) * T + C::KC - 1) / C::KC;
-  // key tile of chunk c: scalar loads, fetched one chunk ahead so their
-  // wait lands where no LDS or vector-memory work is outstanding
+  // first key of chunk c, with bit 31 set when its tile is marked partial:
+  // scalar loads, fetched one chunk ahead so their wait lands where no LDS
+  // or vector-memory work is outstanding
   auto chunk_key0 = [&](int c) {
-    return col_idx[t_begin + c / C::CPT] * T + (c % C::CPT) * C::KC;
+    const int raw = col_idx[t_begin + c / C::CPT];
+    return ((raw & 0x7fffffff) * T + (c % C::CPT) * C::KC) | (raw & int(0x80000000));
   };
+  // this lane's query as (frame, position), for the token predicate
+  const int qi = qrow / mg.s, qa = qrow - (qrow / mg.s) * mg.s;
 
   // Chunk staging by direct global -> LDS copies (no staging registers):
   // copy jj of this wave fills LDS bytes [(wave*NDMA + jj) * 1024, +1024) of
@@ -121,12 +128,12 @@ __global__ __launch_bounds__(T / 32 * 64, 2) void radial_fwd_kernel(
   f32x16 oacc[C::NDB];
 #pragma unroll
   for (int db = 0; db < C::NDB; ++db) oacc[db] = zero16();
-  float m_run = -INFINITY;  // reference max of the log2-scaled logits
+  float m_run = kNoMax;     // reference max of the log2-scaled logits
   float l_run = 0.f;        // this lane's share of the running sum
 
   int key_next = nchunks > 0 ? chunk_key0(0) : 0;            // chunk c + 1
   int key_after = nchunks > 1 ? chunk_key0(1) : 0;           // chunk c + 2
-  if (nchunks > 0) issue_copy(0, key_next);
+  if (nchunks > 0) issue_copy(0, key_next & 0x7fffffff);
   wait_vmem();  // Q fragments and the first chunk
   __syncthreads();
 
@@ -137,10 +144,11 @@ __global__ __launch_bounds__(T / 32 * 64, 2) void radial_fwd_kernel(
   for (int c = 0; c < nchunks; ++c) {
     const bf16 *Ks = lds + (c & 1) * C::BUF;
     const bf16 *Vs = Ks + C::KC * D;
-    const int key0 = key_next;
+    const int key0 = key_next & 0x7fffffff;
+    const bool partial = EXACT && key_next < 0;
     key_next = key_after;
     // the next chunk's copy lands in the other buffer during these products
-    if (c + 1 < nchunks) issue_copy((c + 1) & 1, key_next);
+    if (c + 1 < nchunks) issue_copy((c + 1) & 1, key_next & 0x7fffffff);
     if (c + 2 < nchunks) key_after = chunk_key0(c + 2);
 
     // S^T for the wave's 32 queries against the chunk's KC keys.  The K
@@ -173,6 +181,14 @@ __global__ __launch_bounds__(T / 32 * 64, 2) void radial_fwd_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r)
           if (kb * 32 + 8 * (r >> 2) + (r & 3) >= lim) s[kb][r] = -INFINITY;
+    }
+    if (partial) {  // token-exact: keys outside the query's runs get -inf
+      const unsigned ok = lane_key_bits<C::NKB>(qi, qa, key0, g, mg.s, mg.frames, mg.sink != 0);
+#pragma unroll
+      for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (!((ok >> (16 * kb + r)) & 1u)) s[kb][r] = -INFINITY;
     }
     float mx = -INFINITY;
 #pragma unroll
@@ -251,14 +267,19 @@ __global__ __launch_bounds__(T / 32 * 64, 2) void radial_fwd_kernel(
   }
 }
 
-template <int D, int T>
+template <int D, int T, bool EXACT>
 hipError_t launch_fwd_t(const FwdArgs &a, hipStream_t stream) {
   const int64_t works = (int64_t)a.BH * a.nb;
-  hipLaunchKernelGGL((radial_fwd_kernel<D, T>), dim3((unsigned)works), dim3(FwdCfg<D, T>::NT),
-                     0, stream, (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.v,
-                     (bf16 *)a.o, a.lse, a.row_ptr, a.col_idx, a.N, a.nb, (int32_t)works,
-                     a.scale * kLog2e);
+  hipLaunchKernelGGL((radial_fwd_kernel<D, T, EXACT>), dim3((unsigned)works),
+                     dim3(FwdCfg<D, T>::NT), 0, stream, (const bf16 *)a.q, (const bf16 *)a.k,
+                     (const bf16 *)a.v, (bf16 *)a.o, a.lse, a.row_ptr, a.col_idx, a.N, a.nb,
+                     (int32_t)works, a.scale * kLog2e, a.mask);
   return hipGetLastError();
+}
+
+template <int D, int T>
+hipError_t launch_fwd_t(const FwdArgs &a, hipStream_t stream) {
+  return a.mask.exact ? launch_fwd_t<D, T, true>(a, stream) : launch_fwd_t<D, T, false>(a, stream);
 }
 
 hipError_t launch_fwd(const FwdArgs &a, hipStream_t stream) {

@@ -2,6 +2,7 @@
 // kernel dispatch.  Never throws or aborts across the boundary.
 #include <hip/hip_runtime_api.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstdlib>
@@ -127,6 +128,13 @@ int radial_layout_export(const radial_layout *L, int32_t *row_ptr, int32_t *col_
   return RADIAL_OK;
 }
 
+int radial_layout_tile_flags(const radial_layout *L, uint8_t *csr_full, uint8_t *csc_full) {
+  if (!L) return fail(RADIAL_E_INVALID, "layout is NULL");
+  if (csr_full && L->nnz_tiles) std::copy(L->full.begin(), L->full.end(), csr_full);
+  if (csc_full && L->nnz_tiles) std::copy(L->full_csc.begin(), L->full_csc.end(), csc_full);
+  return RADIAL_OK;
+}
+
 int radial_layout_band_table(const radial_layout *L, int32_t *band, int64_t *width,
                              int64_t *period) {
   if (!L) return fail(RADIAL_E_INVALID, "layout is NULL");
@@ -164,13 +172,27 @@ int radial_layout_upload(radial_layout *L) {
   }
   int32_t *b = static_cast<int32_t *>(p);
   size_t off = 0;
+  // Token-exact layouts mark partial tiles in bit 31 of the device tile
+  // indices (the kernels mask the token predicate inside those tiles only).
+  std::vector<int32_t> col_dev, row_dev;
+  const std::vector<int32_t> *col_src = &L->col_idx, *row_src = &L->row_idx;
+  if ((L->flags & RADIAL_TOKEN_EXACT) && !(L->flags & RADIAL_DENSE)) {
+    col_dev = L->col_idx;
+    row_dev = L->row_idx;
+    for (size_t t = 0; t < nz; ++t) {
+      if (!L->full[t]) col_dev[t] = int32_t(uint32_t(col_dev[t]) | 0x80000000u);
+      if (!L->full_csc[t]) row_dev[t] = int32_t(uint32_t(row_dev[t]) | 0x80000000u);
+    }
+    col_src = &col_dev;
+    row_src = &row_dev;
+  }
   struct Part {
     const std::vector<int32_t> *src;
     const int32_t **dst;
   } parts[] = {{&L->row_ptr, &L->d_row_ptr},
-               {&L->col_idx, &L->d_col_idx},
+               {col_src, &L->d_col_idx},
                {&L->col_ptr, &L->d_col_ptr},
-               {&L->row_idx, &L->d_row_idx},
+               {row_src, &L->d_row_idx},
                {&L->col_order, &L->d_col_order}};
   for (auto &pt : parts) {
     const size_t cnt = pt.src->size();
@@ -194,6 +216,15 @@ void radial_layout_destroy(radial_layout *L) {
   delete L;
 }
 
+static radial::MaskGeom mask_geom(const radial_layout *L) {
+  radial::MaskGeom m;
+  m.s = static_cast<int32_t>(L->tokens_per_frame);
+  m.frames = static_cast<int32_t>(L->frames);
+  m.sink = (L->flags & RADIAL_SINK) ? 1 : 0;
+  m.exact = ((L->flags & RADIAL_TOKEN_EXACT) && !(L->flags & RADIAL_DENSE)) ? 1 : 0;
+  return m;
+}
+
 int radial_attn_fwd(const radial_layout *L, int32_t B, int32_t H, int64_t N, int32_t D,
                     float scale, const void *q, const void *k, const void *v, void *o,
                     float *lse, void *hip_stream) {
@@ -215,6 +246,7 @@ int radial_attn_fwd(const radial_layout *L, int32_t B, int32_t H, int64_t N, int
   a.T = L->block;
   a.nb = L->nb;
   a.scale = scale;
+  a.mask = mask_geom(L);
   const hipError_t e = radial::launch_fwd(a, static_cast<hipStream_t>(hip_stream));
   if (e != hipSuccess)
     return fail(RADIAL_E_HIP, std::string("forward launch failed: ") + hipGetErrorString(e));
@@ -273,6 +305,7 @@ int radial_attn_bwd(const radial_layout *L, int32_t B, int32_t H, int64_t N, int
   a.T = L->block;
   a.nb = L->nb;
   a.scale = scale;
+  a.mask = mask_geom(L);
   const hipError_t e = radial::launch_bwd(a, static_cast<hipStream_t>(hip_stream));
   if (e != hipSuccess)
     return fail(RADIAL_E_HIP, std::string("backward launch failed: ") + hipGetErrorString(e));

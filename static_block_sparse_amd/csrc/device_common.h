@@ -248,6 +248,103 @@ __device__ __forceinline__ void wait_vmem_n() {
   __builtin_amdgcn_s_waitcnt(0x0F70 | n);
 }
 
+// Token predicate of the radial mask as runs (used inside the tiles a
+// token-exact layout marks partial).  For a query at in-frame position a of
+// frame i, the allowed keys of frame j are one run of positions: all of frame
+// 0 with the sink; else, with delta = |i - j|, r = floor(log2(max(delta, 1)))
+// and w = s >> r, the positions b with |a - b| < w, or below unit width
+// (w == 0) the single position a on frame distances that are a multiple of
+// ceil(2^r / s) (review Step 2-A..C and Step 4; paper §4.2 Fig.5, Eq.8).
+// key_run returns that run as [lo, lo + len) in absolute key index (len 0
+// when empty).  The predicate is symmetric in (i, a) and (j, b) except for
+// the sink, which is a key-frame condition: query_run gives the allowed
+// queries of query frame i for the key at position b of frame j.
+__device__ __forceinline__ void band_run(int delta, int pos, int frame, int s, int &lo,
+                                         unsigned &len) {
+  const int r = 31 - __builtin_clz(delta > 1 ? delta : 1);
+  const int w = r < 31 ? (s >> r) : 0;
+  if (w >= 1) {
+    const int b0 = pos - w + 1 > 0 ? pos - w + 1 : 0;
+    const int b1 = pos + w < s ? pos + w : s;
+    lo = frame * s + b0;
+    len = (unsigned)(b1 - b0);
+  } else {
+    const unsigned long long p2 = 1ull << r;
+    const unsigned period = (unsigned)((p2 + (unsigned)s - 1) / (unsigned)s);
+    lo = frame * s + pos;
+    len = ((unsigned)delta % period == 0) ? 1u : 0u;
+  }
+}
+__device__ __forceinline__ void key_run(int qi, int qa, int j, int s, bool sink, int &lo,
+                                        unsigned &len) {
+  if (sink && j == 0) {
+    lo = 0;
+    len = (unsigned)s;
+    return;
+  }
+  band_run(qi > j ? qi - j : j - qi, qa, j, s, lo, len);
+}
+__device__ __forceinline__ void query_run(int kj, int kb, int i, int s, bool sink, int &lo,
+                                          unsigned &len) {
+  if (sink && kj == 0) {
+    lo = i * s;
+    len = (unsigned)s;
+    return;
+  }
+  band_run(kj > i ? kj - i : i - kj, kb, i, s, lo, len);
+}
+
+// x in [lo, lo + len)
+__device__ __forceinline__ bool in_run(int x, int lo, unsigned len) {
+  return (unsigned)(x - lo) < len;
+}
+
+// Allowed-pair bits of one lane over NB 32-wide blocks of a 32 x 32 product
+// result, in the result's register layout: bit 16 kb + r stands for index
+// x0 + 32 kb + 8 (r / 4) + 4 g + r % 4 of the span (g = lane / 32).  The
+// span may cross any number of frames (frames shorter than the span), so
+// the runs of every frame it touches are tested; indices past the last
+// frame get 0.  lane_key_bits: the lane is query (qi, qa), the span is keys;
+// lane_query_bits: the lane is key (kj, kb), the span is queries.
+template <int NB, bool QUERIES>
+__device__ __forceinline__ unsigned lane_pair_bits(int fi, int pos, int x0, int g, int s,
+                                                   int frames, bool sink) {
+  static_assert(NB >= 1 && NB <= 2, "at most 32 bits");
+  const int f0 = x0 / s;
+  int f1 = (x0 + 32 * NB - 1) / s;
+  f1 = f1 < frames - 1 ? f1 : frames - 1;
+  unsigned ok = 0;
+  for (int f = f0; f <= f1; ++f) {
+    int lo;
+    unsigned len;
+    if constexpr (QUERIES)
+      query_run(fi, pos, f, s, sink, lo, len);
+    else
+      key_run(fi, pos, f, s, sink, lo, len);
+    const int b = x0 + 4 * g - lo;
+#pragma unroll
+    for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        ok |= ((unsigned)(b + 32 * kb + 8 * (r >> 2) + (r & 3)) < len ? 1u : 0u) << (16 * kb + r);
+  }
+  return ok;
+}
+template <int NB>
+__device__ __forceinline__ unsigned lane_key_bits(int qi, int qa, int key0, int g, int s,
+                                                  int frames, bool sink) {
+  return lane_pair_bits<NB, false>(qi, qa, key0, g, s, frames, sink);
+}
+__device__ __forceinline__ unsigned lane_query_bits(int kj, int kb, int row0, int g, int s,
+                                                    int frames, bool sink) {
+  return lane_pair_bits<1, true>(kj, kb, row0, g, s, frames, sink);
+}
+
+// A running maximum that starts finite: a row whose first chunks are fully
+// masked (token-exact layouts) then exponentiates -inf - m = -inf to 0
+// instead of -inf + inf = NaN.
+constexpr float kNoMax = -1e30f;
+
 // Work-item order for a launch of n workgroups whose work items are
 // numbered head-major (query tile fastest).  The hardware hands workgroups to
 // the 8 XCDs round robin (workgroup b runs on XCD b % 8).  Work is dealt to

@@ -6,6 +6,15 @@
 
 namespace radial {
 
+// What the kernels need of the mask to apply it token by token inside the
+// tiles a token-exact layout marks partial (bit 31 of the tile indices).
+struct MaskGeom {
+  int32_t s = 1;        // tokens per frame
+  int32_t frames = 1;
+  int32_t sink = 0;     // frame 0 keys always allowed
+  int32_t exact = 0;    // token-exact layout
+};
+
 struct FwdArgs {
   const void *q, *k, *v;
   void *o;
@@ -13,6 +22,7 @@ struct FwdArgs {
   const int32_t *row_ptr, *col_idx;  // device CSR of the layout
   int32_t BH, N, D, T, nb;
   float scale;
+  MaskGeom mask;
 };
 
 struct BwdArgs {
@@ -25,6 +35,7 @@ struct BwdArgs {
   const int32_t *col_order;          // key tiles, longest column first
   int32_t BH, N, D, T, nb;
   float scale;
+  MaskGeom mask;
 };
 
 // Both return hipErrorInvalidValue for an unsupported (D, T) pair.

@@ -22,6 +22,9 @@ struct radial_layout {
   std::vector<int32_t> row_ptr, col_idx;  // CSR: key tiles per query tile
   std::vector<int32_t> col_ptr, row_idx;  // CSC: query tiles per key tile
   std::vector<int32_t> col_order;         // key tiles, longest column first
+  // full[t] = 1 when every valid token pair of CSR tile t is allowed (no
+  // masking needed under token-exact semantics), else 0; full_csc in CSC order
+  std::vector<uint8_t> full, full_csc;
 
   // device copy (one allocation): row_ptr | col_idx | col_ptr | row_idx | col_order
   int device = -1;

@@ -17,7 +17,9 @@
 //     caption);
 //   * attention sink: all of frame 0 is reachable (Step 4; paper Eq.8);
 //   * tiles: a T x T tile is kept iff it holds at least one allowed pair,
-//     and kept tiles are computed in full (Step 5; paper §4.2).
+//     and kept tiles are computed in full (Step 5; paper §4.2).  For
+//     token-exact semantics (paper Eq.4 at token granularity) each kept tile
+//     is also marked full (every valid pair allowed) or partial.
 //
 // Construction: for one query tile, its rows fall into one or more frame
 // segments (frame i, positions a0..a1).  Against key frame j the keys
@@ -26,7 +28,12 @@
 // positions overlap because every run is at least one key wide), or
 // [a0, a1] on the sampled diagonal, or the whole frame for the sink.  Each
 // run maps to a run of key tiles; the union of the runs of a query tile,
-// sorted and merged, is its CSR row.
+// sorted and merged, is its CSR row.  The keys of frame j reachable from
+// *every* position of a segment are [a1 - w + 1, a0 + w - 1] (clipped), the
+// single position a0 on the sampled diagonal when a0 == a1, or the whole
+// frame for the sink; intersected over the tile's segments this gives, per
+// key frame, the keys every query of the tile may attend, and a kept tile
+// whose keys lie inside that set in each of its frames is full.
 #include <algorithm>
 #include <cstdint>
 #include <string>
@@ -67,7 +74,8 @@ std::string build_layout(int64_t frames, int64_t s, int32_t T, uint32_t flags,
   if (frames < 1) return "frames must be >= 1";
   if (s < 1) return "tokens_per_frame must be >= 1";
   if (T < 1 || T > 4096) return "block_size must be in [1, 4096]";
-  if (flags & ~uint32_t(RADIAL_SINK | RADIAL_DENSE)) return "unknown flag bits";
+  if (flags & ~uint32_t(RADIAL_SINK | RADIAL_DENSE | RADIAL_TOKEN_EXACT))
+    return "unknown flag bits";
   if (frames > (int64_t(1) << 31) / s) return "frames * tokens_per_frame must be < 2^31";
   const int64_t n = frames * s;
   if (n >= (int64_t(1) << 31)) return "frames * tokens_per_frame must be < 2^31";
@@ -140,16 +148,68 @@ std::string build_layout(int64_t frames, int64_t s, int32_t T, uint32_t flags,
   L.nnz_tiles = static_cast<int64_t>(L.col_idx.size());
   if (L.nnz_tiles >= (int64_t(1) << 31)) return "too many tiles for 32-bit indices";
 
+  // full / partial kept tiles
+  L.full.assign(L.nnz_tiles, 1);
+  if (!dense) {
+    std::vector<int64_t> clo(frames), chi(frames);  // common keys per key frame, [clo, chi]
+    for (int64_t u = 0; u < nb; ++u) {
+      const int64_t q0 = u * T;
+      const int64_t q1 = std::min(n, q0 + T) - 1;
+      std::fill(clo.begin(), clo.end(), int64_t(0));
+      std::fill(chi.begin(), chi.end(), s - 1);
+      for (int64_t i = q0 / s; i <= q1 / s; ++i) {
+        const int64_t a0 = (i == q0 / s) ? q0 % s : 0;
+        const int64_t a1 = (i == q1 / s) ? q1 % s : s - 1;
+        for (int64_t j = 0; j < frames; ++j) {
+          int64_t lo, hi;
+          if (sink && j == 0) {
+            lo = 0;
+            hi = s - 1;
+          } else {
+            const int64_t delta = i > j ? i - j : j - i;
+            const int64_t w = L.band_w[delta];
+            if (w >= 1) {
+              lo = std::max<int64_t>(0, a1 - w + 1);
+              hi = std::min<int64_t>(s - 1, a0 + w - 1);
+            } else if (a0 == a1 && delta % L.band_period[delta] == 0) {
+              lo = hi = a0;
+            } else {
+              lo = 1;
+              hi = 0;  // empty
+            }
+          }
+          clo[j] = std::max(clo[j], lo);
+          chi[j] = std::min(chi[j], hi);
+        }
+      }
+      for (int32_t t = L.row_ptr[u]; t < L.row_ptr[u + 1]; ++t) {
+        const int64_t k0 = int64_t(L.col_idx[t]) * T;
+        const int64_t k1 = std::min(n, k0 + T) - 1;
+        bool full = true;
+        for (int64_t j = k0 / s; j <= k1 / s && full; ++j) {
+          const int64_t b0 = std::max(k0, j * s) - j * s;
+          const int64_t b1 = std::min(k1, j * s + s - 1) - j * s;
+          full = clo[j] <= b0 && b1 <= chi[j];
+        }
+        L.full[t] = full ? 1 : 0;
+      }
+    }
+  }
+
   // transpose to CSC (query tiles ascending within each key tile)
   L.col_ptr.assign(nb + 1, 0);
   for (int32_t v : L.col_idx) L.col_ptr[v + 1]++;
   for (int64_t v = 0; v < nb; ++v) L.col_ptr[v + 1] += L.col_ptr[v];
   L.row_idx.assign(L.nnz_tiles, 0);
+  L.full_csc.assign(L.nnz_tiles, 1);
   {
     std::vector<int32_t> fill(L.col_ptr.begin(), L.col_ptr.end() - 1);
     for (int64_t u = 0; u < nb; ++u)
-      for (int32_t t = L.row_ptr[u]; t < L.row_ptr[u + 1]; ++t)
-        L.row_idx[fill[L.col_idx[t]]++] = static_cast<int32_t>(u);
+      for (int32_t t = L.row_ptr[u]; t < L.row_ptr[u + 1]; ++t) {
+        const int32_t at = fill[L.col_idx[t]]++;
+        L.row_idx[at] = static_cast<int32_t>(u);
+        L.full_csc[at] = L.full[t];
+      }
   }
 
   // longest columns first for the dK/dV pass (the sink columns of frame 0

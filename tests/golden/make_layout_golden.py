@@ -1,8 +1,9 @@
 """Writes tests/golden/layouts.json from the oracle only.
 
 For every workload shape (and a few small ones) it stores the tile count,
-the valid token pairs inside kept tiles and SHA-256 digests of the CSR and
-CSC arrays as little-endian int32, so the C++ mask compiler can be checked
+the valid token pairs inside kept tiles, SHA-256 digests of the CSR and
+CSC arrays as little-endian int32, and digests of the full-tile marks in
+CSR and CSC order (one byte per kept tile, 1 = every valid pair allowed), so the C++ mask compiler can be checked
 bit-exactly without recomputing the oracle at full size in every test run.
 
 Run from the repository root:  python tests/golden/make_layout_golden.py
@@ -31,6 +32,10 @@ def digest(a):
     return hashlib.sha256(np.ascontiguousarray(a, dtype="<i4").tobytes()).hexdigest()
 
 
+def digest_u8(a):
+    return hashlib.sha256(np.ascontiguousarray(a, dtype=np.uint8).tobytes()).hexdigest()
+
+
 def main():
     out = []
     for f, s, T in SHAPES:
@@ -38,11 +43,15 @@ def main():
             kept = om.kept_tiles(f, s, T, sink)
             rp, ci = om.csr(kept)
             cp, ri = om.csc(kept)
+            full = om.full_tiles(f, s, T, sink)
             out.append(dict(frames=f, tokens_per_frame=s, tile=T, sink=sink,
                             n_blocks=int(kept.shape[0]), nnz_tiles=int(kept.sum()),
                             nnz_pairs=om.tile_pairs(kept, f * s, T),
                             row_ptr=digest(rp), col_idx=digest(ci),
-                            col_ptr=digest(cp), row_idx=digest(ri)))
+                            col_ptr=digest(cp), row_idx=digest(ri),
+                            n_full=int(full.sum()),
+                            csr_full=digest_u8(full[kept]),
+                            csc_full=digest_u8(full.T[kept.T])))
     path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "layouts.json")
     with open(path, "w") as fh:
         json.dump(out, fh, indent=1)

@@ -2,8 +2,8 @@
 
 * the library loads and exports every function include/radial.h declares;
 * the C++ mask compiler matches the oracle bit-exactly (CSR, CSC, band
-  table, token mask, pair count), live on small shapes and through stored
-  oracle digests at the full workload shapes;
+  table, token mask, pair count, full/partial tile marks), live on small
+  shapes and through stored oracle digests at the full workload shapes;
 * argument validation and the allocation-failure hook return the documented
   status codes without touching a GPU.
 """
@@ -94,6 +94,43 @@ def test_tiles_match_oracle_digests_full_size():
         cp, ri = L.csc()
         assert _digest(rp) == g["row_ptr"] and _digest(ci) == g["col_idx"], g
         assert _digest(cp) == g["col_ptr"] and _digest(ri) == g["row_idx"], g
+
+
+# shapes where the sampled diagonal (w = 0) and frame-straddling tiles occur
+FLAG_SHAPES = SMALL + [(600, 3, 16), (40, 1, 8), (129, 20, 16), (70, 5, 9)]
+
+
+@pytest.mark.parametrize("sink", [True, False])
+def test_tile_flags_match_oracle_small(sink):
+    for f, s, T in FLAG_SHAPES:
+        L = sba.Layout(f, s, T, sink=sink)
+        kept = om.kept_tiles(f, s, T, sink)
+        full = om.full_tiles(f, s, T, sink)
+        a, b = L.tile_flags()
+        assert np.array_equal(a, full[kept]), (f, s, T)
+        assert np.array_equal(b, full.T[kept.T]), (f, s, T)
+
+
+def test_tile_flags_match_oracle_digests_full_size():
+    gold = json.load(open(os.path.join(ROOT, "tests", "golden", "layouts.json")))
+    u8 = lambda a: hashlib.sha256(np.ascontiguousarray(a, dtype=np.uint8).tobytes()).hexdigest()
+    for g in gold:
+        L = sba.Layout(g["frames"], g["tokens_per_frame"], g["tile"], sink=g["sink"],
+                       token_exact=True)
+        a, b = L.tile_flags()
+        assert int(a.sum()) == g["n_full"] == int(b.sum()), g
+        assert u8(a) == g["csr_full"] and u8(b) == g["csc_full"], g
+
+
+def test_token_exact_flag_keeps_the_tile_lists():
+    # the flag changes only how kept tiles are computed, not which are kept
+    for f, s, T in [(8, 256, 64), (33, 3, 16), (12, 1, 4)]:
+        a, b = sba.Layout(f, s, T), sba.Layout(f, s, T, token_exact=True)
+        assert a.nnz_tiles == b.nnz_tiles and a.nnz_pairs == b.nnz_pairs
+        for x, y in zip(a.csr() + a.csc(), b.csr() + b.csc()):
+            assert np.array_equal(x, y)
+    d = sba.Layout(7, 50, 32, dense=True, token_exact=True)
+    assert all(x.all() for x in d.tile_flags())
 
 
 def test_dense_flag_keeps_every_tile():
