@@ -26,11 +26,52 @@ with its reason in the design notes):
 * tile semantics: a T x T tile of the n x n mask is kept when at least one
   allowed token pair falls in it, and a kept tile is computed in full (review
   Step 5; paper §4.2: block-wise computation with 128x128 blocks).
+
+Mask variants (the ablations of the rebuttal and the review's Appx C.3
+comparison).  The pages name the knobs but not where they enter the
+formulas; these readings are used (``Variant``):
+
+* central band d (rebuttal "Width of Central Band": frame pairs with
+  |i - j| <= d attend each other in full): the frame distance is shifted,
+  e = max(|i - j| - d + 1, 1), and e takes the place of max(|i - j|, 1) in
+  the band index and the widths.  d = 1 is the default mask (distances 0
+  and 1 share band 0).
+* width scale c = num / den (rebuttal "Width Scale Between Consecutive
+  Bands": the ratio between the widths of consecutive bands): bands keep
+  their doubling extent, r = floor(log2 e), and the half width becomes
+  w = floor(s / c**r); below unit width the sampling period is
+  ceil(c**r / s), so the band's amortised density keeps decaying by c.
+  c = 2 is the default mask.  (Read this way a larger c starves distant
+  frames and a smaller c feeds them, as the rebuttal's explanation of the
+  ablation says.)
+* harmonic-series decay (review 1.3.2, Appx C.3: the diagonal width is
+  inversely proportional to the distance): w = floor(s / e), and below unit
+  width the period is ceil(e / s).  The width scale does not apply.
 """
 
 from __future__ import annotations
 
+from dataclasses import dataclass
+
 import numpy as np
+
+
+@dataclass(frozen=True)
+class Variant:
+    """Mask variant (see the module notes); the defaults give the radial mask."""
+    decay: str = "radial"          # "radial" or "harmonic"
+    central: int = 1               # central band d >= 0
+    scale: tuple = (2, 1)          # width scale c = scale[0] / scale[1] > 1
+
+    def __post_init__(self):
+        if self.decay not in ("radial", "harmonic"):
+            raise ValueError(self.decay)
+        num, den = self.scale
+        if self.central < 0 or den < 1 or num <= den:
+            raise ValueError(self)
+
+
+DEFAULT = Variant()
 
 
 # ----------------------------------------------------------------------------
@@ -44,46 +85,60 @@ def band_index(delta: int) -> int:
     return max(int(delta), 1).bit_length() - 1
 
 
-def band(delta: int, s: int) -> tuple[int, int, int]:
+def band(delta: int, s: int, variant: Variant = DEFAULT) -> tuple[int, int, int]:
     """(r, w, q) for frame distance delta and s tokens per frame.
 
     r: band index; w = floor(s / 2**r): half width of the kept diagonal;
     q: diagonal sampling period, only meaningful when w == 0, where a frame
     pair at distance delta keeps its diagonal iff delta % q == 0, with
     q = ceil(2**r / s).  For w >= 1 the period is 1 (no sampling).
+    A variant replaces max(delta, 1) by the shifted distance e and the base
+    2 of the width by its scale, or takes the harmonic width s / e (module
+    notes); r is always floor(log2 e).
     """
-    r = band_index(delta)
-    w = s // (2 ** r)
+    if delta < 0:
+        raise ValueError("frame distance must be >= 0")
+    e = max(int(delta) - variant.central + 1, 1)
+    r = band_index(e)
+    if variant.decay == "harmonic":
+        num, den = e, 1                     # width divisor e
+    else:
+        num, den = variant.scale[0] ** r, variant.scale[1] ** r   # divisor c**r
+    w = (s * den) // num
     if w >= 1:
         q = 1
     else:
-        q = -(-(2 ** r) // s)  # ceil(2**r / s) in integers
+        q = -(-num // (s * den))  # ceil(divisor / s) in integers
     return r, w, q
 
 
-def band_table(f: int, s: int) -> np.ndarray:
-    """int64 array [f, 3] with (r, w, q) for every frame distance 0..f-1."""
-    return np.array([band(d, s) for d in range(f)], dtype=np.int64).reshape(f, 3)
+def band_table(f: int, s: int, variant: Variant = DEFAULT) -> np.ndarray:
+    """int64 array [f, 3] with (r, w, q) for every frame distance 0..f-1.
+    Periods beyond 2**62 are stored as 2**62 (no distance below f reaches
+    them, so the sampled diagonal of such a band is empty either way)."""
+    cap = 2 ** 62
+    rows = [(r, w, min(q, cap)) for r, w, q in (band(d, s, variant) for d in range(f))]
+    return np.array(rows, dtype=np.int64).reshape(f, 3)
 
 
 # ----------------------------------------------------------------------------
 # Token predicate and brute-force mask (review Step 2-4; paper Eq.4, Eq.8)
 # ----------------------------------------------------------------------------
 
-def allowed(q: int, k: int, s: int, sink: bool = True) -> bool:
+def allowed(q: int, k: int, s: int, sink: bool = True, variant: Variant = DEFAULT) -> bool:
     """True iff query token q may attend key token k (scalar, plain Python)."""
     i, a = divmod(q, s)
     j, b = divmod(k, s)
     if sink and j == 0:
         return True
     delta = abs(i - j)
-    r, w, period = band(delta, s)
+    r, w, period = band(delta, s, variant)
     if w >= 1:
         return abs(a - b) < w
     return a == b and delta % period == 0
 
 
-def token_mask(f: int, s: int, sink: bool = True) -> np.ndarray:
+def token_mask(f: int, s: int, sink: bool = True, variant: Variant = DEFAULT) -> np.ndarray:
     """Brute-force boolean mask [n, n] (n = f*s), True = allowed.
 
     Evaluates the same predicate as ``allowed`` for every pair at once; meant
@@ -95,7 +150,7 @@ def token_mask(f: int, s: int, sink: bool = True) -> np.ndarray:
     idx = np.arange(n)
     i, a = np.divmod(idx, s)
     delta = np.abs(i[:, None] - i[None, :])
-    tab = band_table(f, s)
+    tab = band_table(f, s, variant)
     w = tab[delta, 1]
     period = tab[delta, 2]
     sep = np.abs(a[:, None] - a[None, :])
@@ -107,7 +162,7 @@ def token_mask(f: int, s: int, sink: bool = True) -> np.ndarray:
     return m
 
 
-def closed_form_pairs(f: int, s: int, sink: bool = True) -> int:
+def closed_form_pairs(f: int, s: int, sink: bool = True, variant: Variant = DEFAULT) -> int:
     """Number of allowed token pairs, counted per frame pair in closed form.
 
     For a frame pair at distance delta with half width w >= 1, the number of
@@ -119,7 +174,7 @@ def closed_form_pairs(f: int, s: int, sink: bool = True) -> int:
     frame 0 that the band did not already allow.
     """
     def per_pair(delta: int) -> int:
-        r, w, period = band(delta, s)
+        r, w, period = band(delta, s, variant)
         if w >= 1:
             return s * (2 * w - 1) - w * (w - 1)
         return s if delta % period == 0 else 0
@@ -143,7 +198,8 @@ def n_blocks(n: int, T: int) -> int:
     return -(-n // T)
 
 
-def kept_tiles(f: int, s: int, T: int, sink: bool = True) -> np.ndarray:
+def kept_tiles(f: int, s: int, T: int, sink: bool = True,
+               variant: Variant = DEFAULT) -> np.ndarray:
     """Boolean [nb, nb] tile map: kept[u, v] iff some allowed (q, k) has
     q // T == u and k // T == v.
 
@@ -155,7 +211,7 @@ def kept_tiles(f: int, s: int, T: int, sink: bool = True) -> np.ndarray:
     """
     n = f * s
     nb = n_blocks(n, T)
-    tab = band_table(f, s)
+    tab = band_table(f, s, variant)
     qtok = np.arange(n, dtype=np.int64)
     qi, qa = np.divmod(qtok, s)
     qtile = qtok // T
@@ -220,13 +276,13 @@ def tile_pairs(kept: np.ndarray, n: int, T: int) -> int:
 
 
 def effective_mask(f: int, s: int, T: int, sink: bool = True,
-                   mode: str = "tile") -> np.ndarray:
+                   mode: str = "tile", variant: Variant = DEFAULT) -> np.ndarray:
     """Boolean [n, n] mask the attention uses (small n only).
 
     mode "tile": every token pair inside a kept tile (tile semantics).
     mode "token": exactly the allowed token pairs.
     """
-    tok = token_mask(f, s, sink)
+    tok = token_mask(f, s, sink, variant)
     if mode == "token":
         return tok
     if mode != "tile":
@@ -244,7 +300,8 @@ def effective_mask(f: int, s: int, T: int, sink: bool = True,
 # it; a tile in which every valid token pair is allowed needs no masking.
 # ----------------------------------------------------------------------------
 
-def full_tiles(f: int, s: int, T: int, sink: bool = True) -> np.ndarray:
+def full_tiles(f: int, s: int, T: int, sink: bool = True,
+               variant: Variant = DEFAULT) -> np.ndarray:
     """Boolean [nb, nb] tile map: full[u, v] iff tile (u, v) is kept and every
     token pair (q, k) in it with q, k < n is allowed.
 
@@ -256,8 +313,8 @@ def full_tiles(f: int, s: int, T: int, sink: bool = True) -> np.ndarray:
     """
     n = f * s
     nb = n_blocks(n, T)
-    tab = band_table(f, s)
-    kept = kept_tiles(f, s, T, sink)
+    tab = band_table(f, s, variant)
+    kept = kept_tiles(f, s, T, sink, variant)
     full = np.zeros_like(kept)
     q = np.arange(n, dtype=np.int64)
     qi, qa = np.divmod(q, s)
@@ -304,7 +361,8 @@ def full_tiles_bruteforce(mask: np.ndarray, T: int) -> np.ndarray:
     return allowed_all & kept_tiles_bruteforce(mask, T)
 
 
-def token_mask_rows(f: int, s: int, rows: np.ndarray, sink: bool = True) -> np.ndarray:
+def token_mask_rows(f: int, s: int, rows: np.ndarray, sink: bool = True,
+                    variant: Variant = DEFAULT) -> np.ndarray:
     """Boolean [len(rows), n]: the token predicate for the given query rows
     against every key (the same predicate as ``allowed``, vectorised)."""
     n = f * s
@@ -313,7 +371,7 @@ def token_mask_rows(f: int, s: int, rows: np.ndarray, sink: bool = True) -> np.n
     i, a = np.divmod(rows, s)
     j, b = np.divmod(keys, s)
     delta = np.abs(i[:, None] - j[None, :])
-    tab = band_table(f, s)
+    tab = band_table(f, s, variant)
     w = tab[delta, 1]
     period = tab[delta, 2]
     sep = np.abs(a[:, None] - b[None, :])
