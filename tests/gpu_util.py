@@ -25,7 +25,11 @@ Tolerances (forward, bf16 inputs, fp32 accumulation):
 * Gradients: dQ, dK, dV are rounded to bf16 and built from bf16-rounded P
   and dS, the same error structure as O, so the same relative guards apply
   against rms of the reference gradient, together with the absolute bounds
-  on values normalised by max(1, rms(ref)).
+  on values normalised by max(1, rms(ref)).  No tolerance is stated for
+  gradients, and elements of several units (keys every query attends, in
+  masks whose rows hold few keys) carry a bf16 rounding near the max-abs
+  bound by themselves, so for gradients the max-abs bound applies after the
+  element-wise allowance below.
 * Peaky softmax gradients (logit std ~8): the backward receives O rounded to
   bf16, so Delta = rowsum(dO * O) is off by up to
   eps ~ 2^-9 * sum_d |dO| |O| ~ 2^-9 * sqrt(D) ~ 0.02 per row (3 sigma ~0.06)
@@ -63,12 +67,15 @@ def check_close(got: np.ndarray, ref: np.ndarray, what: str, absolute: bool = Tr
     rms = float(np.sqrt(np.mean(ref ** 2)))
     stats = dict(max_abs=float(err.max()), mean_abs=float(err.mean()), rms_ref=rms)
     norm = max(1.0, rms) if normalise else 1.0
+    excess = float((err - ELEM_REL * np.abs(ref)).max())
+    stats["max_excess"] = excess
     if absolute:
-        assert stats["max_abs"] / norm <= O_MAX_ABS, (what, stats)
+        # O: the stated max-abs target as is; gradients (normalise=True):
+        # the same bound after the element-wise rounding allowance
+        top = excess if normalise else stats["max_abs"]
+        assert top / norm <= O_MAX_ABS, (what, stats)
         assert stats["mean_abs"] / norm <= O_MEAN_ABS, (what, stats)
     if rms > 0:
-        excess = float((err - ELEM_REL * np.abs(ref)).max())
-        stats["max_excess"] = excess
         assert excess <= rel_max * rms, (what, stats)
         assert stats["mean_abs"] <= rel_mean * rms, (what, stats)
     return stats
