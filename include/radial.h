@@ -68,6 +68,37 @@ enum {
 
 typedef struct radial_layout radial_layout; /* opaque */
 
+/* ---- mask variants ------------------------------------------------------
+   Knobs of the rebuttal's ablations and the review's harmonic-series
+   comparison (review 1.3.2, Appx C.3).  The pages name them but not where
+   they enter the formulas; the readings below are used.  With the frame
+   distance delta = |i - j|, the shifted distance is
+     e = max(delta - central_band + 1, 1)
+   (rebuttal "Width of Central Band": frame pairs with delta <= d attend in
+   full), the band index is r = floor(log2(e)) and the half width w and the
+   sampling period p (used when w == 0) are
+     RADIAL_DECAY_RADIAL:   w = floor(s / c^r), p = ceil(c^r / s), where
+                            c = scale_num / scale_den is the ratio between
+                            consecutive bands' widths (rebuttal "Width Scale
+                            Between Consecutive Bands"); bands keep their
+                            doubling extent;
+     RADIAL_DECAY_HARMONIC: w = floor(s / e), p = ceil(e / s) (width
+                            inversely proportional to the distance); the
+                            scale is ignored.
+   The defaults (radial, d = 1, c = 2/1) give the mask described at
+   radial_mask_build. */
+enum { RADIAL_DECAY_RADIAL = 0, RADIAL_DECAY_HARMONIC = 1 };
+
+typedef struct radial_mask_params {
+  int32_t decay;        /* RADIAL_DECAY_RADIAL or RADIAL_DECAY_HARMONIC           */
+  int32_t central_band; /* d >= 0                                                  */
+  int32_t scale_num;    /* c = scale_num / scale_den; 1 <= scale_den <= 4,         */
+  int32_t scale_den;    /*   scale_den < scale_num <= 16 (checked for radial only) */
+} radial_mask_params;
+
+/* Fills *p with the defaults (radial decay, d = 1, c = 2/1). */
+void radial_mask_params_default(radial_mask_params *p);
+
 /*
  * radial_mask_build -- compile the radial mask of a video with `frames`
  * frames of `tokens_per_frame` tokens (n = frames * tokens_per_frame) into
@@ -98,6 +129,14 @@ typedef struct radial_layout radial_layout; /* opaque */
 int radial_mask_build(int64_t frames, int64_t tokens_per_frame, int32_t block_size,
                       uint32_t flags, radial_layout **out);
 
+/* radial_mask_build for a mask variant (see radial_mask_params); params ==
+   NULL means the defaults, i.e. radial_mask_build.  RADIAL_E_INVALID for
+   parameters outside the stated ranges.  Every other call works on the
+   resulting layout unchanged, token-exact semantics included. */
+int radial_mask_build_ex(int64_t frames, int64_t tokens_per_frame, int32_t block_size,
+                         uint32_t flags, const radial_mask_params *params,
+                         radial_layout **out);
+
 /* Sizes of a layout.  n_tokens = frames * tokens_per_frame; n_blocks =
    ceil(n / block_size); nnz_tiles = kept tiles; nnz_pairs = token pairs
    inside kept tiles, counting only rows and columns < n (the work the
@@ -121,7 +160,8 @@ int radial_layout_tile_flags(const radial_layout *L, uint8_t *csr_full, uint8_t 
 
 /* Band table, one entry per frame distance delta in [0, frames):
    band[delta] = r, width[delta] = w, period[delta] = sampling period
-   (1 when w >= 1).  Any pointer may be NULL. */
+   (1 when w >= 1; capped at 2^31 - 1, beyond every frame distance).  Any
+   pointer may be NULL. */
 int radial_layout_band_table(const radial_layout *L, int32_t *band, int64_t *width,
                              int64_t *period);
 

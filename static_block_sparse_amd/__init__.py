@@ -21,13 +21,19 @@ import os
 import numpy as np
 
 __all__ = ["Layout", "attn_fwd", "attn_bwd", "lib", "LIB_PATH", "SINK", "DENSE",
-           "TOKEN_EXACT", "RadialError"]
+           "TOKEN_EXACT", "DECAYS", "RadialError"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libradial.so")
 
 SINK = 1
 DENSE = 2
 TOKEN_EXACT = 4
+DECAYS = {"radial": 0, "harmonic": 1}
+
+
+class _MaskParams(ctypes.Structure):
+    _fields_ = [("decay", ctypes.c_int32), ("central_band", ctypes.c_int32),
+                ("scale_num", ctypes.c_int32), ("scale_den", ctypes.c_int32)]
 
 _STATUS = {0: "RADIAL_OK", -1: "RADIAL_E_INVALID", -2: "RADIAL_E_UNSUPPORTED",
            -3: "RADIAL_E_SHAPE", -4: "RADIAL_E_NOMEM", -5: "RADIAL_E_HIP", -6: "RADIAL_E_STATE"}
@@ -47,6 +53,8 @@ def _declare(L):
     P = c.POINTER
     sigs = {
         "radial_mask_build": (c.c_int, [i64, i64, i32, u32, P(vp)]),
+        "radial_mask_build_ex": (c.c_int, [i64, i64, i32, u32, P(_MaskParams), P(vp)]),
+        "radial_mask_params_default": (None, [P(_MaskParams)]),
         "radial_layout_info": (c.c_int, [vp, P(i64), P(i32), P(i64), P(i64)]),
         "radial_layout_export": (c.c_int, [vp, vp, vp, vp, vp]),
         "radial_layout_tile_flags": (c.c_int, [vp, vp, vp]),
@@ -89,13 +97,24 @@ class Layout:
 
     ``token_exact=False`` (the default) computes every kept tile in full;
     ``token_exact=True`` masks the tiles the mask only partly covers token by
-    token, so the attention follows the token mask exactly."""
+    token, so the attention follows the token mask exactly.
+
+    Mask variants (include/radial.h, radial_mask_params): ``decay`` "radial"
+    or "harmonic", ``central_band`` d (frame pairs with |i - j| <= d attend in
+    full) and ``width_scale`` (num, den), the ratio between consecutive
+    bands' widths; the defaults give the radial mask."""
 
     def __init__(self, frames: int, tokens_per_frame: int, block_size: int = 128,
-                 sink: bool = True, dense: bool = False, token_exact: bool = False):
+                 sink: bool = True, dense: bool = False, token_exact: bool = False,
+                 decay: str = "radial", central_band: int = 1, width_scale=(2, 1)):
         flags = (SINK if sink else 0) | (DENSE if dense else 0) | (TOKEN_EXACT if token_exact else 0)
+        if decay not in DECAYS:
+            raise ValueError(f"decay must be one of {sorted(DECAYS)}")
+        prm = _MaskParams(DECAYS[decay], int(central_band), int(width_scale[0]),
+                          int(width_scale[1]))
         h = ctypes.c_void_p()
-        _check(lib().radial_mask_build(frames, tokens_per_frame, block_size, flags, ctypes.byref(h)))
+        _check(lib().radial_mask_build_ex(frames, tokens_per_frame, block_size, flags,
+                                          ctypes.byref(prm), ctypes.byref(h)))
         self._h = h
         self.frames = frames
         self.tokens_per_frame = tokens_per_frame
@@ -103,6 +122,9 @@ class Layout:
         self.sink = sink
         self.dense = dense
         self.token_exact = token_exact
+        self.decay = decay
+        self.central_band = int(central_band)
+        self.width_scale = (int(width_scale[0]), int(width_scale[1]))
         n, nb, nz, pairs = ctypes.c_int64(), ctypes.c_int32(), ctypes.c_int64(), ctypes.c_int64()
         _check(lib().radial_layout_info(h, ctypes.byref(n), ctypes.byref(nb), ctypes.byref(nz),
                                         ctypes.byref(pairs)))

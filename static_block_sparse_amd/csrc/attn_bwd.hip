@@ -142,6 +142,11 @@ __global__ __launch_bounds__(T / 32 * 64, 1) void radial_bwd_dkdv_kernel(
   const bool k_ok = key < N;
   // this lane's key as (frame, position), for the token predicate
   const int kj = key / mg.s, kpos = key - (key / mg.s) * mg.s;
+  // token-exact: the mask's per-band table, read by the predicate from LDS
+  __shared__ int lds_rtab[64];
+  int rtab_v = 0;
+  if constexpr (EXACT) rtab_v = tid < 64 ? mg.band_rtab[tid] : 0;
+  const BandCtx bctx{mg.s, mg.frames, mg.central, mg.sink != 0, mg.decay == 1, lds_rtab};
   bf16x8 kf[C::NKK], vf[C::NKK];
 #pragma unroll
   for (int kk = 0; kk < C::NKK; ++kk) {
@@ -317,8 +322,7 @@ __global__ __launch_bounds__(T / 32 * 64, 1) void radial_bwd_dkdv_kernel(
     } else {
       const int meta = lds_meta[b];
       if (meta >= 0) return ~0u;
-      return lane_query_bits(kj, kpos, (meta & 0x7fffffff) + 32 * m, g, mg.s, mg.frames,
-                             mg.sink != 0);
+      return lane_query_bits(bctx, kj, kpos, (meta & 0x7fffffff) + 32 * m, g);
     }
   };
 
@@ -330,6 +334,9 @@ __global__ __launch_bounds__(T / 32 * 64, 1) void radial_bwd_dkdv_kernel(
     wait_vmem_n<C::NCOPY>();
   } else {
     wait_vmem();
+  }
+  if constexpr (EXACT) {
+    if (tid < 64) lds_rtab[tid] = rtab_v;
   }
   __syncthreads();
   int row_c = nch > 2 ? row0_of(2) : 0;
@@ -462,6 +469,10 @@ __global__ __launch_bounds__(T / 32 * 64, 2) void radial_bwd_dq_kernel(
   };
   // this lane's query as (frame, position), for the token predicate
   const int qi = qrow / mg.s, qa = qrow - (qrow / mg.s) * mg.s;
+  // token-exact: the mask's per-band table, read by the predicate from LDS
+  __shared__ int lds_rtab[64];
+  int rtab_v = 0;
+  if constexpr (EXACT) rtab_v = threadIdx.x < 64 ? mg.band_rtab[threadIdx.x] : 0;
 
   typename C::Copier cp;
   cp.init(wave, lane);
@@ -475,7 +486,11 @@ __global__ __launch_bounds__(T / 32 * 64, 2) void radial_bwd_dq_kernel(
   int key_nn = nch > 1 ? key_of(1) : 0;
   if (nch > 0) issue(0, key_n & 0x7fffffff);
   wait_vmem();  // Q, dO fragments, LSE, Delta and the first chunk
+  if constexpr (EXACT) {
+    if (threadIdx.x < 64) lds_rtab[threadIdx.x] = rtab_v;
+  }
   __syncthreads();
+  const BandCtx bctx{mg.s, mg.frames, mg.central, mg.sink != 0, mg.decay == 1, lds_rtab};
 
   for (int c = 0; c < nch; ++c) {
     const int key0 = key_n & 0x7fffffff;
@@ -484,7 +499,7 @@ __global__ __launch_bounds__(T / 32 * 64, 2) void radial_bwd_dq_kernel(
     const int key_3 = c + 2 < nch ? key_of(c + 2) : 0;
     // token-exact: this lane's allowed keys of the chunk
     const unsigned ok =
-        partial ? lane_key_bits<C::NKB>(qi, qa, key0, g, mg.s, mg.frames, mg.sink != 0) : ~0u;
+        partial ? lane_key_bits<C::NKB>(bctx, qi, qa, key0, g) : ~0u;
     const bf16 *Ks = lds + (c & 1) * 2 * C::CHUNK;
     const bf16 *Vs = Ks + C::CHUNK;
 

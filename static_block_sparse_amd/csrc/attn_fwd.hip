@@ -79,6 +79,10 @@ __global__ __launch_bounds__(T / 32 * 64, 2) void radial_fwd_kernel(
 
   const int qrow = u * T + wave * 32 + c32;
   const bool q_ok = qrow < N;
+  // token-exact: the mask's per-band table, read by the predicate from LDS
+  __shared__ int lds_rtab[64];
+  int rtab_v = 0;
+  if constexpr (EXACT) rtab_v = tid < 64 ? mg.band_rtab[tid] : 0;
   bf16x8 qf[C::NKK];
 #pragma unroll
   for (int kk = 0; kk < C::NKK; ++kk)
@@ -135,7 +139,11 @@ __global__ __launch_bounds__(T / 32 * 64, 2) void radial_fwd_kernel(
   int key_after = nchunks > 1 ? chunk_key0(1) : 0;           // chunk c + 2
   if (nchunks > 0) issue_copy(0, key_next & 0x7fffffff);
   wait_vmem();  // Q fragments and the first chunk
+  if constexpr (EXACT) {
+    if (tid < 64) lds_rtab[tid] = rtab_v;
+  }
   __syncthreads();
+  const BandCtx bctx{mg.s, mg.frames, mg.central, mg.sink != 0, mg.decay == 1, lds_rtab};
 
   // lane (g, c32) in transposing-read group G = lane / 16 addresses row
   // n0 + j / 4 and columns d0 + 4 (j % 4), j = lane % 16
@@ -183,7 +191,7 @@ __global__ __launch_bounds__(T / 32 * 64, 2) void radial_fwd_kernel(
           if (kb * 32 + 8 * (r >> 2) + (r & 3) >= lim) s[kb][r] = -INFINITY;
     }
     if (partial) {  // token-exact: keys outside the query's runs get -inf
-      const unsigned ok = lane_key_bits<C::NKB>(qi, qa, key0, g, mg.s, mg.frames, mg.sink != 0);
+      const unsigned ok = lane_key_bits<C::NKB>(bctx, qi, qa, key0, g);
 #pragma unroll
       for (int kb = 0; kb < C::NKB; ++kb)
 #pragma unroll

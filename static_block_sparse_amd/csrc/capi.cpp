@@ -42,6 +42,7 @@ void free_device(radial_layout *L) {
   }
   L->d_base = nullptr;
   L->d_row_ptr = L->d_col_idx = L->d_col_ptr = L->d_row_idx = L->d_col_order = nullptr;
+  L->d_band_rtab = nullptr;
   L->device = -1;
 }
 
@@ -83,15 +84,29 @@ int check_ptrs(std::initializer_list<std::pair<const void *, const char *>> ptrs
 
 extern "C" {
 
+void radial_mask_params_default(radial_mask_params *p) {
+  if (p) *p = radial_mask_params{RADIAL_DECAY_RADIAL, 1, 2, 1};
+}
+
 int radial_mask_build(int64_t frames, int64_t tokens_per_frame, int32_t block_size,
                       uint32_t flags, radial_layout **out) {
+  return radial_mask_build_ex(frames, tokens_per_frame, block_size, flags, nullptr, out);
+}
+
+int radial_mask_build_ex(int64_t frames, int64_t tokens_per_frame, int32_t block_size,
+                         uint32_t flags, const radial_mask_params *params,
+                         radial_layout **out) {
   if (!out) return fail(RADIAL_E_INVALID, "out is NULL");
+  radial_mask_params prm;
+  radial_mask_params_default(&prm);
+  if (params) prm = *params;
   *out = nullptr;
   if (forced_alloc_failure()) return fail(RADIAL_E_NOMEM, "allocation failure (forced by test hook)");
   radial_layout *L = new (std::nothrow) radial_layout();
   if (!L) return fail(RADIAL_E_NOMEM, "out of host memory");
   try {
-    const std::string err = radial::build_layout(frames, tokens_per_frame, block_size, flags, *L);
+    const std::string err =
+        radial::build_layout(frames, tokens_per_frame, block_size, flags, prm, *L);
     if (!err.empty()) {
       delete L;
       return fail(RADIAL_E_INVALID, err);
@@ -164,7 +179,7 @@ int radial_layout_upload(radial_layout *L) {
   if (L->d_base) free_device(L);
   if (forced_alloc_failure()) return fail(RADIAL_E_NOMEM, "allocation failure (forced by test hook)");
   const size_t nb1 = (size_t)L->nb + 1, nz = (size_t)L->nnz_tiles, nb = (size_t)L->nb;
-  const size_t words = 2 * nb1 + 2 * nz + nb;
+  const size_t words = 2 * nb1 + 2 * nz + nb + L->band_rtab.size();
   void *p = nullptr;
   if (hipMalloc(&p, words * sizeof(int32_t)) != hipSuccess || !p) {
     (void)hipGetLastError();
@@ -193,7 +208,8 @@ int radial_layout_upload(radial_layout *L) {
                {col_src, &L->d_col_idx},
                {&L->col_ptr, &L->d_col_ptr},
                {row_src, &L->d_row_idx},
-               {&L->col_order, &L->d_col_order}};
+               {&L->col_order, &L->d_col_order},
+               {&L->band_rtab, &L->d_band_rtab}};
   for (auto &pt : parts) {
     const size_t cnt = pt.src->size();
     if (cnt && hipMemcpy(b + off, pt.src->data(), cnt * sizeof(int32_t),
@@ -222,6 +238,9 @@ static radial::MaskGeom mask_geom(const radial_layout *L) {
   m.frames = static_cast<int32_t>(L->frames);
   m.sink = (L->flags & RADIAL_SINK) ? 1 : 0;
   m.exact = ((L->flags & RADIAL_TOKEN_EXACT) && !(L->flags & RADIAL_DENSE)) ? 1 : 0;
+  m.decay = L->params.decay;
+  m.central = L->params.central_band;
+  m.band_rtab = L->d_band_rtab;
   return m;
 }
 

@@ -248,50 +248,66 @@ __device__ __forceinline__ void wait_vmem_n() {
   __builtin_amdgcn_s_waitcnt(0x0F70 | n);
 }
 
-// Token predicate of the radial mask as runs (used inside the tiles a
-// token-exact layout marks partial).  For a query at in-frame position a of
-// frame i, the allowed keys of frame j are one run of positions: all of frame
-// 0 with the sink; else, with delta = |i - j|, r = floor(log2(max(delta, 1)))
-// and w = s >> r, the positions b with |a - b| < w, or below unit width
-// (w == 0) the single position a on frame distances that are a multiple of
-// ceil(2^r / s) (review Step 2-A..C and Step 4; paper §4.2 Fig.5, Eq.8).
-// key_run returns that run as [lo, lo + len) in absolute key index (len 0
+// Token predicate of the mask as runs (used inside the tiles a token-exact
+// layout marks partial).  For a query at in-frame position a of frame i, the
+// allowed keys of frame j are one run of positions: all of frame 0 with the
+// sink; else, with delta = |i - j|, the shifted distance
+// e = max(delta - d + 1, 1) for the central band d, and the band's half
+// width w, the positions b with |a - b| < w, or below unit width (w == 0)
+// the single position a on frame distances that are a multiple of the
+// band's period (review Step 2-A..C and Step 4; paper §4.2 Fig.5, Eq.8;
+// the central band and width scale of the rebuttal's ablations; the
+// harmonic-series width of review Appx C.3).  The radial decay's w and
+// period depend on r = floor(log2 e) only and come from a 32-entry table;
+// the harmonic decay's are w = s / e and period = ceil(e / s).
+// key_run returns the run as [lo, lo + len) in absolute key index (len 0
 // when empty).  The predicate is symmetric in (i, a) and (j, b) except for
 // the sink, which is a key-frame condition: query_run gives the allowed
 // queries of query frame i for the key at position b of frame j.
-__device__ __forceinline__ void band_run(int delta, int pos, int frame, int s, int &lo,
-                                         unsigned &len) {
-  const int r = 31 - __builtin_clz(delta > 1 ? delta : 1);
-  const int w = r < 31 ? (s >> r) : 0;
+struct BandCtx {
+  int s, frames, central;
+  bool sink, harmonic;
+  const int *rtab;  // width of band r at [r], period at [32 + r]
+};
+__device__ __forceinline__ void band_run(const BandCtx &c, int delta, int pos, int frame,
+                                         int &lo, unsigned &len) {
+  const int e = delta - c.central + 1 > 1 ? delta - c.central + 1 : 1;
+  int w, period;
+  if (c.harmonic) {
+    w = c.s / e;
+    period = w >= 1 ? 1 : (e - 1) / c.s + 1;
+  } else {
+    const int r = 31 - __builtin_clz(e);
+    w = c.rtab[r];
+    period = c.rtab[32 + r];
+  }
   if (w >= 1) {
-    const int b0 = pos - w + 1 > 0 ? pos - w + 1 : 0;
-    const int b1 = pos + w < s ? pos + w : s;
-    lo = frame * s + b0;
+    const int b0 = pos >= w ? pos - w + 1 : 0;
+    const int b1 = w < c.s - pos ? pos + w : c.s;
+    lo = frame * c.s + b0;
     len = (unsigned)(b1 - b0);
   } else {
-    const unsigned long long p2 = 1ull << r;
-    const unsigned period = (unsigned)((p2 + (unsigned)s - 1) / (unsigned)s);
-    lo = frame * s + pos;
-    len = ((unsigned)delta % period == 0) ? 1u : 0u;
+    lo = frame * c.s + pos;
+    len = (delta % period == 0) ? 1u : 0u;
   }
 }
-__device__ __forceinline__ void key_run(int qi, int qa, int j, int s, bool sink, int &lo,
+__device__ __forceinline__ void key_run(const BandCtx &c, int qi, int qa, int j, int &lo,
                                         unsigned &len) {
-  if (sink && j == 0) {
+  if (c.sink && j == 0) {
     lo = 0;
-    len = (unsigned)s;
+    len = (unsigned)c.s;
     return;
   }
-  band_run(qi > j ? qi - j : j - qi, qa, j, s, lo, len);
+  band_run(c, qi > j ? qi - j : j - qi, qa, j, lo, len);
 }
-__device__ __forceinline__ void query_run(int kj, int kb, int i, int s, bool sink, int &lo,
+__device__ __forceinline__ void query_run(const BandCtx &c, int kj, int kb, int i, int &lo,
                                           unsigned &len) {
-  if (sink && kj == 0) {
-    lo = i * s;
-    len = (unsigned)s;
+  if (c.sink && kj == 0) {
+    lo = i * c.s;
+    len = (unsigned)c.s;
     return;
   }
-  band_run(kj > i ? kj - i : i - kj, kb, i, s, lo, len);
+  band_run(c, kj > i ? kj - i : i - kj, kb, i, lo, len);
 }
 
 // x in [lo, lo + len)
@@ -307,20 +323,20 @@ __device__ __forceinline__ bool in_run(int x, int lo, unsigned len) {
 // frame get 0.  lane_key_bits: the lane is query (qi, qa), the span is keys;
 // lane_query_bits: the lane is key (kj, kb), the span is queries.
 template <int NB, bool QUERIES>
-__device__ __forceinline__ unsigned lane_pair_bits(int fi, int pos, int x0, int g, int s,
-                                                   int frames, bool sink) {
+__device__ __forceinline__ unsigned lane_pair_bits(const BandCtx &c, int fi, int pos, int x0,
+                                                   int g) {
   static_assert(NB >= 1 && NB <= 2, "at most 32 bits");
-  const int f0 = x0 / s;
-  int f1 = (x0 + 32 * NB - 1) / s;
-  f1 = f1 < frames - 1 ? f1 : frames - 1;
+  const int f0 = x0 / c.s;
+  int f1 = (x0 + 32 * NB - 1) / c.s;
+  f1 = f1 < c.frames - 1 ? f1 : c.frames - 1;
   unsigned ok = 0;
   for (int f = f0; f <= f1; ++f) {
     int lo;
     unsigned len;
     if constexpr (QUERIES)
-      query_run(fi, pos, f, s, sink, lo, len);
+      query_run(c, fi, pos, f, lo, len);
     else
-      key_run(fi, pos, f, s, sink, lo, len);
+      key_run(c, fi, pos, f, lo, len);
     const int b = x0 + 4 * g - lo;
 #pragma unroll
     for (int kb = 0; kb < NB; ++kb)
@@ -331,13 +347,13 @@ __device__ __forceinline__ unsigned lane_pair_bits(int fi, int pos, int x0, int 
   return ok;
 }
 template <int NB>
-__device__ __forceinline__ unsigned lane_key_bits(int qi, int qa, int key0, int g, int s,
-                                                  int frames, bool sink) {
-  return lane_pair_bits<NB, false>(qi, qa, key0, g, s, frames, sink);
+__device__ __forceinline__ unsigned lane_key_bits(const BandCtx &c, int qi, int qa, int key0,
+                                                  int g) {
+  return lane_pair_bits<NB, false>(c, qi, qa, key0, g);
 }
-__device__ __forceinline__ unsigned lane_query_bits(int kj, int kb, int row0, int g, int s,
-                                                    int frames, bool sink) {
-  return lane_pair_bits<1, true>(kj, kb, row0, g, s, frames, sink);
+__device__ __forceinline__ unsigned lane_query_bits(const BandCtx &c, int kj, int kb, int row0,
+                                                    int g) {
+  return lane_pair_bits<1, true>(c, kj, kb, row0, g);
 }
 
 // A running maximum that starts finite: a row whose first chunks are fully

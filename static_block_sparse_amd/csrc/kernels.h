@@ -13,6 +13,11 @@ struct MaskGeom {
   int32_t frames = 1;
   int32_t sink = 0;     // frame 0 keys always allowed
   int32_t exact = 0;    // token-exact layout
+  int32_t decay = 0;    // RADIAL_DECAY_RADIAL (0) or RADIAL_DECAY_HARMONIC (1)
+  int32_t central = 1;  // central band d
+  // device: per band index r < 32, width at [r] and period at [32 + r]
+  // (radial decay)
+  const int32_t *band_rtab = nullptr;
 };
 
 struct FwdArgs {

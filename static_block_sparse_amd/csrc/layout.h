@@ -5,12 +5,15 @@
 #include <string>
 #include <vector>
 
+#include "radial.h"
+
 struct radial_layout {
   int64_t frames = 0;
   int64_t tokens_per_frame = 0;
   int64_t n = 0;           // frames * tokens_per_frame
   int32_t block = 0;       // tile edge T
   uint32_t flags = 0;
+  radial_mask_params params{RADIAL_DECAY_RADIAL, 1, 2, 1};
   int32_t nb = 0;          // ceil(n / T)
   int64_t nnz_tiles = 0;
   int64_t nnz_pairs = 0;
@@ -18,6 +21,9 @@ struct radial_layout {
   std::vector<int32_t> band_r;      // per frame distance
   std::vector<int64_t> band_w;
   std::vector<int64_t> band_period;
+  // per band index r in [0, 32): w at [r], period at [32 + r] (radial decay;
+  // what the device predicate looks up)
+  std::vector<int32_t> band_rtab;
 
   std::vector<int32_t> row_ptr, col_idx;  // CSR: key tiles per query tile
   std::vector<int32_t> col_ptr, row_idx;  // CSC: query tiles per key tile
@@ -26,7 +32,8 @@ struct radial_layout {
   // masking needed under token-exact semantics), else 0; full_csc in CSC order
   std::vector<uint8_t> full, full_csc;
 
-  // device copy (one allocation): row_ptr | col_idx | col_ptr | row_idx | col_order
+  // device copy (one allocation): row_ptr | col_idx | col_ptr | row_idx |
+  // col_order | band_rtab
   int device = -1;
   void *d_base = nullptr;
   const int32_t *d_row_ptr = nullptr;
@@ -34,6 +41,7 @@ struct radial_layout {
   const int32_t *d_col_ptr = nullptr;
   const int32_t *d_row_idx = nullptr;
   const int32_t *d_col_order = nullptr;
+  const int32_t *d_band_rtab = nullptr;
 };
 
 namespace radial {
@@ -41,7 +49,7 @@ namespace radial {
 // Fills everything above except the device copy.  Returns an empty string
 // on success, else a description of what was invalid.
 std::string build_layout(int64_t frames, int64_t tokens_per_frame, int32_t block,
-                         uint32_t flags, radial_layout &L);
+                         uint32_t flags, const radial_mask_params &params, radial_layout &L);
 
 // Token predicate of the layout's mask (tests only).
 bool token_allowed(const radial_layout &L, int64_t q, int64_t k);

@@ -15,6 +15,10 @@
 //     for frame pairs whose distance is a multiple of ceil(2^r / s), which
 //     keeps the band's amortised density near 2^-r (Step 2-C; paper Fig.5
 //     caption);
+//   * mask variants (rebuttal ablations; review 1.3.2 / Appx C.3): the
+//     distance is shifted by the central band d, e = max(delta - d + 1, 1),
+//     r = floor(log2 e), and the width divisor 2^r becomes c^r for a width
+//     scale c, or e for the harmonic-series decay (the period likewise);
 //   * attention sink: all of frame 0 is reachable (Step 4; paper Eq.8);
 //   * tiles: a T x T tile is kept iff it holds at least one allowed pair,
 //     and kept tiles are computed in full (Step 5; paper §4.2).  For
@@ -54,24 +58,53 @@ struct Band {
   int64_t period;
 };
 
-inline Band band_of(int64_t delta, int64_t s) {
-  Band b;
-  b.r = bit_length(static_cast<uint64_t>(delta < 1 ? 1 : delta)) - 1;
-  b.w = (b.r >= 63) ? 0 : (s >> b.r);
+// sampling periods beyond every frame distance are stored as this
+constexpr int64_t kPeriodCap = (int64_t(1) << 31) - 1;
+
+using u128 = unsigned __int128;
+
+inline u128 pow_u128(u128 b, int e) {
+  u128 x = 1;
+  while (e-- > 0) x *= b;
+  return x;
+}
+
+// Width and period of a band whose width divisor is num / den (exact
+// rational arithmetic: num <= 16^31 < 2^128, s * den <= 2^31 * 4^31 < 2^128).
+inline void width_of(u128 num, u128 den, int64_t s, Band &b) {
+  const u128 sd = u128(s) * den;
+  b.w = static_cast<int64_t>(sd / num);
   if (b.w >= 1) {
     b.period = 1;
   } else {
-    const int64_t p2 = int64_t(1) << b.r;  // r <= 62 here since delta < 2^63
-    b.period = (p2 + s - 1) / s;
+    const u128 q = (num + sd - 1) / sd;
+    b.period = q > u128(kPeriodCap) ? kPeriodCap : static_cast<int64_t>(q);
   }
+}
+
+inline Band band_of(int64_t delta, int64_t s, const radial_mask_params &p) {
+  const int64_t e = std::max<int64_t>(delta - p.central_band + 1, 1);
+  Band b;
+  b.r = bit_length(static_cast<uint64_t>(e)) - 1;
+  if (p.decay == RADIAL_DECAY_HARMONIC)
+    width_of(u128(e), 1, s, b);
+  else
+    width_of(pow_u128(u128(p.scale_num), b.r), pow_u128(u128(p.scale_den), b.r), s, b);
   return b;
 }
 
 }  // namespace
 
 std::string build_layout(int64_t frames, int64_t s, int32_t T, uint32_t flags,
-                         radial_layout &L) {
+                         const radial_mask_params &params, radial_layout &L) {
   if (frames < 1) return "frames must be >= 1";
+  if (params.decay != RADIAL_DECAY_RADIAL && params.decay != RADIAL_DECAY_HARMONIC)
+    return "unknown decay";
+  if (params.central_band < 0) return "central_band must be >= 0";
+  if (params.decay == RADIAL_DECAY_RADIAL &&
+      (params.scale_den < 1 || params.scale_den > 4 || params.scale_num <= params.scale_den ||
+       params.scale_num > 16))
+    return "width scale must be num/den with 1 <= den <= 4 and den < num <= 16";
   if (s < 1) return "tokens_per_frame must be >= 1";
   if (T < 1 || T > 4096) return "block_size must be in [1, 4096]";
   if (flags & ~uint32_t(RADIAL_SINK | RADIAL_DENSE | RADIAL_TOKEN_EXACT))
@@ -87,6 +120,7 @@ std::string build_layout(int64_t frames, int64_t s, int32_t T, uint32_t flags,
   L.n = n;
   L.block = T;
   L.flags = flags;
+  L.params = params;
   const int64_t nb = (n + T - 1) / T;
   L.nb = static_cast<int32_t>(nb);
 
@@ -94,10 +128,19 @@ std::string build_layout(int64_t frames, int64_t s, int32_t T, uint32_t flags,
   L.band_w.resize(frames);
   L.band_period.resize(frames);
   for (int64_t d = 0; d < frames; ++d) {
-    const Band b = band_of(d, s);
+    const Band b = band_of(d, s, params);
     L.band_r[d] = b.r;
     L.band_w[d] = b.w;
     L.band_period[d] = b.period;
+  }
+  // per band index: the radial decay's width depends on r alone
+  L.band_rtab.assign(64, 0);
+  for (int r = 0; r < 32; ++r) {
+    Band b;
+    width_of(pow_u128(u128(params.scale_num > 0 ? params.scale_num : 2), r),
+             pow_u128(u128(params.scale_den > 0 ? params.scale_den : 1), r), s, b);
+    L.band_rtab[r] = static_cast<int32_t>(b.w);
+    L.band_rtab[32 + r] = static_cast<int32_t>(b.period);
   }
 
   L.row_ptr.assign(nb + 1, 0);

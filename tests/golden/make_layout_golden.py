@@ -1,6 +1,7 @@
 """Writes tests/golden/layouts.json from the oracle only.
 
-For every workload shape (and a few small ones) it stores the tile count,
+For every workload shape (and a few small ones), and for the mask variants
+of the ablations at the 720p shape, it stores the tile count,
 the valid token pairs inside kept tiles, SHA-256 digests of the CSR and
 CSC arrays as little-endian int32, and digests of the full-tile marks in
 CSR and CSC order (one byte per kept tile, 1 = every valid pair allowed), so the C++ mask compiler can be checked
@@ -36,6 +37,28 @@ def digest_u8(a):
     return hashlib.sha256(np.ascontiguousarray(a, dtype=np.uint8).tobytes()).hexdigest()
 
 
+# mask variants of the ablations, at the 720p shape and a small one (sink on)
+VARIANT_SHAPES = [(33, 3600, 128), (8, 256, 64)]
+VARIANTS = [om.Variant(central=0), om.Variant(central=2), om.Variant(scale=(3, 2)),
+            om.Variant(scale=(3, 1)), om.Variant(scale=(4, 1)), om.Variant(decay="harmonic")]
+
+
+def entry(f, s, T, sink, v):
+    kept = om.kept_tiles(f, s, T, sink, v)
+    rp, ci = om.csr(kept)
+    cp, ri = om.csc(kept)
+    full = om.full_tiles(f, s, T, sink, v)
+    return dict(frames=f, tokens_per_frame=s, tile=T, sink=sink,
+                variant=dict(decay=v.decay, central=v.central, scale=list(v.scale)),
+                n_blocks=int(kept.shape[0]), nnz_tiles=int(kept.sum()),
+                nnz_pairs=om.tile_pairs(kept, f * s, T),
+                row_ptr=digest(rp), col_idx=digest(ci),
+                col_ptr=digest(cp), row_idx=digest(ri),
+                n_full=int(full.sum()),
+                csr_full=digest_u8(full[kept]),
+                csc_full=digest_u8(full.T[kept.T]))
+
+
 def main():
     out = []
     for f, s, T in SHAPES:
@@ -52,6 +75,9 @@ def main():
                             n_full=int(full.sum()),
                             csr_full=digest_u8(full[kept]),
                             csc_full=digest_u8(full.T[kept.T])))
+    for f, s, T in VARIANT_SHAPES:
+        for v in VARIANTS:
+            out.append(entry(f, s, T, True, v))
     path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "layouts.json")
     with open(path, "w") as fh:
         json.dump(out, fh, indent=1)

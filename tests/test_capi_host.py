@@ -84,10 +84,19 @@ def _digest(a):
     return hashlib.sha256(np.ascontiguousarray(a, dtype="<i4").tobytes()).hexdigest()
 
 
+def _variant_kwargs(g):
+    v = g.get("variant")
+    if v is None:
+        return {}
+    return dict(decay=v["decay"], central_band=v["central"], width_scale=tuple(v["scale"]))
+
+
 def test_tiles_match_oracle_digests_full_size():
     gold = json.load(open(os.path.join(ROOT, "tests", "golden", "layouts.json")))
+    assert sum(1 for g in gold if "variant" in g) >= 12
     for g in gold:
-        L = sba.Layout(g["frames"], g["tokens_per_frame"], g["tile"], sink=g["sink"])
+        L = sba.Layout(g["frames"], g["tokens_per_frame"], g["tile"], sink=g["sink"],
+                       **_variant_kwargs(g))
         assert L.n_blocks == g["n_blocks"] and L.nnz_tiles == g["nnz_tiles"]
         assert L.nnz_pairs == g["nnz_pairs"]
         rp, ci = L.csr()
@@ -116,7 +125,7 @@ def test_tile_flags_match_oracle_digests_full_size():
     u8 = lambda a: hashlib.sha256(np.ascontiguousarray(a, dtype=np.uint8).tobytes()).hexdigest()
     for g in gold:
         L = sba.Layout(g["frames"], g["tokens_per_frame"], g["tile"], sink=g["sink"],
-                       token_exact=True)
+                       token_exact=True, **_variant_kwargs(g))
         a, b = L.tile_flags()
         assert int(a.sum()) == g["n_full"] == int(b.sum()), g
         assert u8(a) == g["csr_full"] and u8(b) == g["csc_full"], g
@@ -131,6 +140,59 @@ def test_token_exact_flag_keeps_the_tile_lists():
             assert np.array_equal(x, y)
     d = sba.Layout(7, 50, 32, dense=True, token_exact=True)
     assert all(x.all() for x in d.tile_flags())
+
+
+VARIANTS = [om.Variant(central=0), om.Variant(central=2), om.Variant(scale=(3, 2)),
+            om.Variant(scale=(3, 1)), om.Variant(scale=(4, 1)), om.Variant(decay="harmonic"),
+            om.Variant(decay="harmonic", central=2), om.Variant(central=3, scale=(5, 2)),
+            om.Variant(central=50)]
+
+
+def _layout(f, s, T, sink, v, **kw):
+    return sba.Layout(f, s, T, sink=sink, decay=v.decay, central_band=v.central,
+                      width_scale=v.scale, **kw)
+
+
+@pytest.mark.parametrize("variant", VARIANTS, ids=str)
+def test_variants_match_oracle_small(variant):
+    cap = 2 ** 31 - 1
+    for f, s, T in [(4, 9, 4), (8, 256, 64), (5, 7, 3), (33, 3, 16), (12, 1, 4), (40, 2, 7),
+                    (20, 33, 32), (17, 100, 64), (600, 3, 16), (70, 5, 9)]:
+        for sink in (True, False):
+            L = _layout(f, s, T, sink, variant)
+            kept = om.kept_tiles(f, s, T, sink, variant)
+            rp, ci = om.csr(kept)
+            cp, ri = om.csc(kept)
+            assert all(np.array_equal(a, b) for a, b in zip(L.csr() + L.csc(), (rp, ci, cp, ri))), \
+                (f, s, T, sink)
+            assert L.nnz_pairs == om.tile_pairs(kept, f * s, T)
+            full = om.full_tiles(f, s, T, sink, variant)
+            a, b = L.tile_flags()
+            assert np.array_equal(a, full[kept]) and np.array_equal(b, full.T[kept.T])
+            r, w, p = L.band_table()
+            tab = om.band_table(f, s, variant)
+            assert np.array_equal(r, tab[:, 0]) and np.array_equal(w, tab[:, 1])
+            assert np.array_equal(p, np.minimum(tab[:, 2], cap))
+            if f * s <= 700:
+                assert np.array_equal(L.token_mask(), om.token_mask(f, s, sink, variant))
+
+
+@pytest.mark.parametrize("prm", [(2, 1, 2, 1), (0, -1, 2, 1), (0, 1, 2, 2), (0, 1, 1, 2),
+                                 (0, 1, 17, 1), (0, 1, 10, 5), (0, 1, 2, 0)])
+def test_build_ex_rejects_bad_variants(prm):
+    P = sba._MaskParams(*prm)
+    h = ctypes.c_void_p(123)
+    assert sba.lib().radial_mask_build_ex(8, 64, 16, 1, ctypes.byref(P), ctypes.byref(h)) == -1
+    assert h.value is None
+    # the harmonic decay ignores the scale; NULL params are the defaults
+    P = sba._MaskParams(1, 1, 0, 0)
+    assert sba.lib().radial_mask_build_ex(8, 64, 16, 1, ctypes.byref(P), ctypes.byref(h)) == 0
+    sba.lib().radial_layout_destroy(h)
+    assert sba.lib().radial_mask_build_ex(8, 64, 16, 1, None, ctypes.byref(h)) == 0
+    sba.lib().radial_layout_destroy(h)
+    d = sba._MaskParams(9, 9, 9, 9)
+    sba.lib().radial_mask_params_default(ctypes.byref(d))
+    assert (d.decay, d.central_band, d.scale_num, d.scale_den) == (0, 1, 2, 1)
 
 
 def test_dense_flag_keeps_every_tile():
