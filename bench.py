@@ -24,7 +24,10 @@ head, divided by the measured step time.  Extra objects:
   dense        -- the same kernel on an all-tiles layout (dense attention);
   bwd          -- the backward pass (dQ, dK, dV) on the same workload;
   token_exact  -- forward and backward with token-exact masking inside the
-                  partly covered tiles (same kept tiles, same flop count).
+                  partly covered tiles (same kept tiles, same flop count);
+  variants     -- the mask variants of the ablations (central band d, width
+                  scale c, harmonic-series decay) on the same workload:
+                  their tiles, density and forward/backward times.
 """
 
 from __future__ import annotations
@@ -43,7 +46,11 @@ sys.path.insert(0, ROOT)
 METRIC = "radial attn fwd latency (ms) + effective TFLOP/s on nonzero tiles vs bf16 peak"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
-FWD_SOURCES = ["attn_fwd.hip", "device_common.h"]
+FWD_SOURCES = ["attn_fwd.hip", "device_common.h", "kernels.h"]
+# mask variants of the ablations (central band d, width scale c, decay)
+VARIANTS = [("d=0", dict(central_band=0)), ("d=2", dict(central_band=2)),
+            ("c=1.5", dict(width_scale=(3, 2))), ("c=3", dict(width_scale=(3, 1))),
+            ("c=4", dict(width_scale=(4, 1))), ("harmonic", dict(decay="harmonic"))]
 
 
 def log(*a):
@@ -148,7 +155,7 @@ def main():
     ap.add_argument("--workload", default="hunyuan_5s_720p")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the dense and backward legs")
-    ap.add_argument("--only", choices=["fwd", "bwd", "dense", "exact", "copy"],
+    ap.add_argument("--only", choices=["fwd", "bwd", "dense", "exact", "variants", "copy"],
                     help="run only one leg (for profiler runs); prints no JSON")
     args = ap.parse_args()
 
@@ -253,7 +260,7 @@ def main():
 
     bflops = 10 * w.D * L.nnz_pairs * BH
     do = ws = None
-    if args.only in (None, "bwd", "exact") and not args.no_extras:
+    if args.only in (None, "bwd", "exact", "variants") and not args.no_extras:
         g = torch.Generator(dev).manual_seed(w.seed + 1000)
         do = torch.randn(q.shape, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
         ws = torch.empty(sba.lib().radial_attn_bwd_workspace_bytes(L.handle, w.B, w.H, w.N, w.D),
@@ -305,6 +312,37 @@ def main():
                 result["token_exact"]["bwd_overhead_vs_tile_mode"] = round(
                     xb / result["bwd"]["ms"] - 1, 4)
         del Lx
+
+    if args.only in (None, "variants") and not args.no_extras:
+        rows = []
+        st = 2 if args.only is None else args.steps
+        for name, kw in VARIANTS:
+            Lv = sba.Layout(w.frames, w.tokens_per_frame, w.T, sink=True, **kw)
+            Lv.upload(dev)
+            vf = 4 * w.D * Lv.nnz_pairs * BH
+            vb = 10 * w.D * Lv.nnz_pairs * BH
+
+            def vfwd():
+                sba.attn_fwd(q, k, v, Lv, w.scale, out=o, lse=lse)
+
+            def vbwd():
+                sba.attn_bwd(q, k, v, o, lse, do, Lv, w.scale, workspace=ws)
+
+            total_ms, _ = time_launches(vfwd, st, 1)
+            f_ms = total_ms / st
+            vfwd()
+            total_ms, _ = time_launches(vbwd, st, 1)
+            b_ms = total_ms / st
+            dens = Lv.nnz_tiles / Lv.n_blocks ** 2
+            log(f"variant {name}: tiles {Lv.nnz_tiles} (density {dens:.4f}), fwd {f_ms:.2f} ms "
+                f"({vf / f_ms / 1e9:.0f} TFLOP/s), bwd {b_ms:.2f} ms ({vb / b_ms / 1e9:.0f} TFLOP/s)")
+            rows.append({"variant": name, "nnz_tiles_per_head": Lv.nnz_tiles,
+                         "tile_density": round(dens, 5), "fwd_ms": round(f_ms, 3),
+                         "fwd_tflops": round(vf / f_ms / 1e9, 2), "bwd_ms": round(b_ms, 3),
+                         "bwd_tflops": round(vb / b_ms / 1e9, 2)})
+            del Lv
+        if result is not None:
+            result["variants"] = rows
 
     if result is None:
         return

@@ -158,6 +158,20 @@ int radial_layout_export(const radial_layout *L, int32_t *row_ptr, int32_t *col_
    Any pointer may be NULL. */
 int radial_layout_tile_flags(const radial_layout *L, uint8_t *csr_full, uint8_t *csc_full);
 
+/* ---- layer / step schedule ---------------------------------------------
+   radial_schedule_dense -- whether layer `layer` at denoising step `step`
+   should attend in full, i.e. be called with a RADIAL_DENSE layout instead
+   of the radial one (rebuttal "Capability of Capturing Long-Range
+   Dependencies" and "Ablations on Initial Full-Attention Layers and
+   Steps": the first two layers stay dense in training and inference, and
+   the first 12 of 50 steps (default-length videos) or 2 steps (4x longer
+   videos) are a dense warm-up at inference).  Returns 1 (dense) when
+   layer < dense_layers or step < warmup_steps, else 0 (radial);
+   RADIAL_E_INVALID when any argument is negative.  Training has no
+   warm-up: pass warmup_steps = 0.  Host only. */
+int radial_schedule_dense(int32_t layer, int32_t step, int32_t dense_layers,
+                          int32_t warmup_steps);
+
 /* Band table, one entry per frame distance delta in [0, frames):
    band[delta] = r, width[delta] = w, period[delta] = sampling period
    (1 when w >= 1; capped at 2^31 - 1, beyond every frame distance).  Any

@@ -20,7 +20,7 @@ import os
 
 import numpy as np
 
-__all__ = ["Layout", "attn_fwd", "attn_bwd", "lib", "LIB_PATH", "SINK", "DENSE",
+__all__ = ["Layout", "Schedule", "attn_fwd", "attn_bwd", "lib", "LIB_PATH", "SINK", "DENSE",
            "TOKEN_EXACT", "DECAYS", "RadialError"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libradial.so")
@@ -59,6 +59,7 @@ def _declare(L):
         "radial_layout_export": (c.c_int, [vp, vp, vp, vp, vp]),
         "radial_layout_tile_flags": (c.c_int, [vp, vp, vp]),
         "radial_layout_band_table": (c.c_int, [vp, vp, vp, vp]),
+        "radial_schedule_dense": (c.c_int, [i32, i32, i32, i32]),
         "radial_layout_token_mask": (c.c_int, [vp, vp, i64]),
         "radial_layout_upload": (c.c_int, [vp]),
         "radial_layout_destroy": (None, [vp]),
@@ -185,6 +186,56 @@ class Layout:
                 _check(lib().radial_layout_upload(self._h))
             self._device = dev
         return self
+
+
+class Schedule:
+    """Per-call choice between the radial layout and the dense one (the
+    first ``dense_layers`` layers, and at inference the first
+    ``warmup_steps`` denoising steps, attend in full; radial_schedule_dense
+    in include/radial.h).  Both layouts are built once and reused; the
+    keyword arguments other than the schedule's go to the radial Layout.
+
+        S = Schedule(33, 3600, dense_layers=2, warmup_steps=12)
+        o, lse = S.fwd(q, k, v, layer=l, step=t)      # step=None: training
+    """
+
+    def __init__(self, frames: int, tokens_per_frame: int, block_size: int = 128,
+                 dense_layers: int = 2, warmup_steps: int = 0, **layout_kwargs):
+        if dense_layers < 0 or warmup_steps < 0:
+            raise ValueError("dense_layers and warmup_steps must be >= 0")
+        self.dense_layers = int(dense_layers)
+        self.warmup_steps = int(warmup_steps)
+        self.radial = Layout(frames, tokens_per_frame, block_size, **layout_kwargs)
+        self.dense = Layout(frames, tokens_per_frame, block_size, dense=True,
+                            sink=layout_kwargs.get("sink", True))
+
+    def is_dense(self, layer: int, step: int | None = None) -> bool:
+        warm = 0 if step is None else self.warmup_steps
+        st = lib().radial_schedule_dense(int(layer), 0 if step is None else int(step),
+                                         self.dense_layers, warm)
+        if st < 0:
+            _check(st)
+        return st == 1
+
+    def layout(self, layer: int, step: int | None = None) -> Layout:
+        return self.dense if self.is_dense(layer, step) else self.radial
+
+    def fwd(self, q, k, v, layer: int, step: int | None = None, **kw):
+        return attn_fwd(q, k, v, self.layout(layer, step), **kw)
+
+    def bwd(self, q, k, v, o, lse, do, layer: int, step: int | None = None, **kw):
+        return attn_bwd(q, k, v, o, lse, do, self.layout(layer, step), **kw)
+
+    def pairs(self, n_layers: int, n_steps: int | None = None) -> int:
+        """Token pairs computed per batch and head over a whole run of
+        n_layers layers x n_steps steps (one pass if n_steps is None)."""
+        steps = [None] if n_steps is None else range(n_steps)
+        return sum(self.layout(l, t).nnz_pairs for l in range(n_layers) for t in steps)
+
+    def density(self, n_layers: int, n_steps: int | None = None) -> float:
+        """Computed share of all token pairs over the run (1.0 = all dense)."""
+        units = n_layers * (1 if n_steps is None else n_steps)
+        return self.pairs(n_layers, n_steps) / (units * self.radial.n ** 2)
 
 
 def _check_qkv(name, t, ref=None):

@@ -146,7 +146,7 @@ __global__ __launch_bounds__(T / 32 * 64, 1) void radial_bwd_dkdv_kernel(
   __shared__ int lds_rtab[64];
   int rtab_v = 0;
   if constexpr (EXACT) rtab_v = tid < 64 ? mg.band_rtab[tid] : 0;
-  const BandCtx bctx{mg.s, mg.frames, mg.central, mg.sink != 0, mg.decay == 1, lds_rtab};
+  const BandCtx bctx = make_band_ctx(mg, lds_rtab);
   bf16x8 kf[C::NKK], vf[C::NKK];
 #pragma unroll
   for (int kk = 0; kk < C::NKK; ++kk) {
@@ -490,7 +490,7 @@ __global__ __launch_bounds__(T / 32 * 64, 2) void radial_bwd_dq_kernel(
     if (threadIdx.x < 64) lds_rtab[threadIdx.x] = rtab_v;
   }
   __syncthreads();
-  const BandCtx bctx{mg.s, mg.frames, mg.central, mg.sink != 0, mg.decay == 1, lds_rtab};
+  const BandCtx bctx = make_band_ctx(mg, lds_rtab);
 
   for (int c = 0; c < nch; ++c) {
     const int key0 = key_n & 0x7fffffff;
@@ -500,6 +500,7 @@ __global__ __launch_bounds__(T / 32 * 64, 2) void radial_bwd_dq_kernel(
     // token-exact: this lane's allowed keys of the chunk
     const unsigned ok =
         partial ? lane_key_bits<C::NKB>(bctx, qi, qa, key0, g) : ~0u;
+    const bool masked = partial && __ballot(ok != ~0u);  // some key of the block is masked
     const bf16 *Ks = lds + (c & 1) * 2 * C::CHUNK;
     const bf16 *Vs = Ks + C::CHUNK;
 
@@ -518,7 +519,7 @@ __global__ __launch_bounds__(T / 32 * 64, 2) void radial_bwd_dq_kernel(
         dp = mfma32(va[kk], dof[kk], dp);
       }
       // register r holds key kb*32 + 8*(r/4) + 4g + r%4 of the chunk
-      if (partial) {
+      if (masked) {
 #pragma unroll
         for (int r = 0; r < 16; ++r)
           if (!((ok >> (16 * kb + r)) & 1u)) s[r] = -INFINITY;

@@ -143,7 +143,7 @@ __global__ __launch_bounds__(T / 32 * 64, 2) void radial_fwd_kernel(
     if (tid < 64) lds_rtab[tid] = rtab_v;
   }
   __syncthreads();
-  const BandCtx bctx{mg.s, mg.frames, mg.central, mg.sink != 0, mg.decay == 1, lds_rtab};
+  const BandCtx bctx = make_band_ctx(mg, lds_rtab);
 
   // lane (g, c32) in transposing-read group G = lane / 16 addresses row
   // n0 + j / 4 and columns d0 + 4 (j % 4), j = lane % 16
@@ -192,11 +192,13 @@ __global__ __launch_bounds__(T / 32 * 64, 2) void radial_fwd_kernel(
     }
     if (partial) {  // token-exact: keys outside the query's runs get -inf
       const unsigned ok = lane_key_bits<C::NKB>(bctx, qi, qa, key0, g);
+      if (__ballot(ok != ~0u)) {  // some key of the wave's block is masked
 #pragma unroll
-      for (int kb = 0; kb < C::NKB; ++kb)
+        for (int kb = 0; kb < C::NKB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (!((ok >> (16 * kb + r)) & 1u)) s[kb][r] = -INFINITY;
+          for (int r = 0; r < 16; ++r)
+            if (!((ok >> (16 * kb + r)) & 1u)) s[kb][r] = -INFINITY;
+      }
     }
     float mx = -INFINITY;
 #pragma unroll

@@ -150,6 +150,13 @@ int radial_layout_tile_flags(const radial_layout *L, uint8_t *csr_full, uint8_t 
   return RADIAL_OK;
 }
 
+int radial_schedule_dense(int32_t layer, int32_t step, int32_t dense_layers,
+                          int32_t warmup_steps) {
+  if (layer < 0 || step < 0 || dense_layers < 0 || warmup_steps < 0)
+    return fail(RADIAL_E_INVALID, "schedule arguments must be >= 0");
+  return (layer < dense_layers || step < warmup_steps) ? 1 : 0;
+}
+
 int radial_layout_band_table(const radial_layout *L, int32_t *band, int64_t *width,
                              int64_t *period) {
   if (!L) return fail(RADIAL_E_INVALID, "layout is NULL");
@@ -241,6 +248,20 @@ static radial::MaskGeom mask_geom(const radial_layout *L) {
   m.decay = L->params.decay;
   m.central = L->params.central_band;
   m.band_rtab = L->d_band_rtab;
+  const radial_mask_params &p = L->params;
+  m.pow2_shift = -1;
+  if (p.decay == RADIAL_DECAY_RADIAL && p.scale_den > 0 && p.scale_num % p.scale_den == 0) {
+    const int32_t c = p.scale_num / p.scale_den;
+    if ((c & (c - 1)) == 0) m.pow2_shift = 31 - __builtin_clz(uint32_t(c));
+  }
+  // division by s for dividends below 2^31: p = 31 + ceil(log2 s) and
+  // m = ceil(2^p / s) (< 2^33) give floor(x / s) = (x m) >> p exactly,
+  // since x (m s - 2^p) < 2^31 s <= 2^p
+  const uint64_t sv = uint64_t(L->tokens_per_frame);
+  int lg = 0;
+  while ((uint64_t(1) << lg) < sv) ++lg;
+  m.s_shift = 31 + lg;
+  m.s_magic = ((uint64_t(1) << m.s_shift) + sv - 1) / sv;
   return m;
 }
 

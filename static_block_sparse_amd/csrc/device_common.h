@@ -24,6 +24,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "kernels.h"
+
 namespace radial {
 
 typedef __bf16 bf16;
@@ -268,25 +270,39 @@ struct BandCtx {
   int s, frames, central;
   bool sink, harmonic;
   const int *rtab;  // width of band r at [r], period at [32 + r]
+  int kshift;       // scale 2^kshift: width s >> (kshift r) directly; else -1
+  unsigned long long smagic;  // x / s == (x * smagic) >> sshift, 0 <= x < 2^31
+  int sshift;
+  __device__ __forceinline__ int div_s(int x) const {
+    return (int)(((unsigned long long)(unsigned)x * smagic) >> sshift);
+  }
 };
+__device__ __forceinline__ BandCtx make_band_ctx(const MaskGeom &mg, const int *rtab) {
+  return BandCtx{mg.s,     mg.frames,     mg.central,  mg.sink != 0, mg.decay == 1,
+                 rtab,     mg.pow2_shift, mg.s_magic,  mg.s_shift};
+}
 __device__ __forceinline__ void band_run(const BandCtx &c, int delta, int pos, int frame,
                                          int &lo, unsigned &len) {
   const int e = delta - c.central + 1 > 1 ? delta - c.central + 1 : 1;
-  int w, period;
+  int w, r = 0;
   if (c.harmonic) {
     w = c.s / e;
-    period = w >= 1 ? 1 : (e - 1) / c.s + 1;
   } else {
-    const int r = 31 - __builtin_clz(e);
-    w = c.rtab[r];
-    period = c.rtab[32 + r];
+    r = 31 - __builtin_clz(e);
+    if (c.kshift >= 0) {
+      const int sh = c.kshift * r;
+      w = sh < 31 ? (c.s >> sh) : 0;
+    } else {
+      w = c.rtab[r];
+    }
   }
   if (w >= 1) {
     const int b0 = pos >= w ? pos - w + 1 : 0;
     const int b1 = w < c.s - pos ? pos + w : c.s;
     lo = frame * c.s + b0;
     len = (unsigned)(b1 - b0);
-  } else {
+  } else {  // below unit width: the sampled diagonal
+    const int period = c.harmonic ? c.div_s(e - 1) + 1 : c.rtab[32 + r];
     lo = frame * c.s + pos;
     len = (delta % period == 0) ? 1u : 0u;
   }
@@ -322,12 +338,20 @@ __device__ __forceinline__ bool in_run(int x, int lo, unsigned len) {
 // the runs of every frame it touches are tested; indices past the last
 // frame get 0.  lane_key_bits: the lane is query (qi, qa), the span is keys;
 // lane_query_bits: the lane is key (kj, kb), the span is queries.
+// Bits of the lane elements whose offset is below y (see lane_pair_bits):
+// 4 per 8 offsets, i.e. 4 floor(y / 8) + min(y % 8, 4) of them.
+template <int NB>
+__device__ __forceinline__ unsigned rank_mask(int y) {
+  y = y < 0 ? 0 : (y > 32 * NB ? 32 * NB : y);
+  const int k = 4 * (y >> 3) + ((y & 7) < 4 ? (y & 7) : 4);
+  return k >= 32 ? ~0u : (1u << k) - 1u;
+}
 template <int NB, bool QUERIES>
 __device__ __forceinline__ unsigned lane_pair_bits(const BandCtx &c, int fi, int pos, int x0,
                                                    int g) {
   static_assert(NB >= 1 && NB <= 2, "at most 32 bits");
-  const int f0 = x0 / c.s;
-  int f1 = (x0 + 32 * NB - 1) / c.s;
+  const int f0 = c.div_s(x0);
+  int f1 = c.div_s(x0 + 32 * NB - 1);
   f1 = f1 < c.frames - 1 ? f1 : c.frames - 1;
   unsigned ok = 0;
   for (int f = f0; f <= f1; ++f) {
@@ -337,12 +361,11 @@ __device__ __forceinline__ unsigned lane_pair_bits(const BandCtx &c, int fi, int
       query_run(c, fi, pos, f, lo, len);
     else
       key_run(c, fi, pos, f, lo, len);
-    const int b = x0 + 4 * g - lo;
-#pragma unroll
-    for (int kb = 0; kb < NB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        ok |= ((unsigned)(b + 32 * kb + 8 * (r >> 2) + (r & 3)) < len ? 1u : 0u) << (16 * kb + r);
+    // the lane's elements sit at offsets 32 kb + 8 (r / 4) + r % 4 from
+    // x0 + 4 g, ascending with the bit index, so a run covers the bits
+    // between the counts of elements below its two ends
+    const int b = x0 + 4 * g;
+    ok |= rank_mask<NB>(lo + (int)len - b) & ~rank_mask<NB>(lo - b);
   }
   return ok;
 }

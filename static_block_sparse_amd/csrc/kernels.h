@@ -18,6 +18,12 @@ struct MaskGeom {
   // device: per band index r < 32, width at [r] and period at [32 + r]
   // (radial decay)
   const int32_t *band_rtab = nullptr;
+  // radial decay with a width scale 2^pow2_shift: the width is s >> (k r)
+  // without the table; -1 for other scales
+  int32_t pow2_shift = 1;
+  // x / s == (x * s_magic) >> s_shift for 0 <= x < 2^31
+  uint64_t s_magic = uint64_t(1) << 31;
+  int32_t s_shift = 31;
 };
 
 struct FwdArgs {
