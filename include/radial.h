@@ -211,7 +211,8 @@ int radial_attn_fwd(const radial_layout *L, int32_t B, int32_t H, int64_t N, int
                     float scale, const void *q, const void *k, const void *v, void *o,
                     float *lse, void *hip_stream);
 
-/* Workspace bytes radial_attn_bwd needs for these sizes (fp32 row terms). */
+/* Workspace bytes radial_attn_bwd needs for these sizes: two fp32 row
+   arrays, -Delta and -LSE * log2(e) (2 * B * H * N floats, rounded up). */
 size_t radial_attn_bwd_workspace_bytes(const radial_layout *L, int32_t B, int32_t H,
                                        int64_t N, int32_t D);
 
@@ -220,8 +221,9 @@ size_t radial_attn_bwd_workspace_bytes(const radial_layout *L, int32_t B, int32_
  * gradient dout = dL/dO: dq, dk, dv (bf16 [B, H, N, D], fully overwritten).
  * o and lse must be the forward's outputs for the same q, k, v, scale and
  * layout.  The probabilities are recomputed from lse; Delta = rowsum(dO*O)
- * is formed first in `workspace` (caller-owned device memory of at least
- * radial_attn_bwd_workspace_bytes bytes, 16-byte aligned).  Deterministic:
+ * and the exponent's row term are formed first in `workspace` (caller-owned
+ * device memory of at least radial_attn_bwd_workspace_bytes bytes, 16-byte
+ * aligned).  Deterministic:
  * no atomics, fixed summation order.
  */
 int radial_attn_bwd(const radial_layout *L, int32_t B, int32_t H, int64_t N, int32_t D,

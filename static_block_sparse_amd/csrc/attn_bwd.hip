@@ -9,10 +9,12 @@
 //   dV = P^T dO,  dP = dO V^T,  dS = P * (dP - Delta)
 //   dK = scale * dS^T Q,  dQ = scale * dS K
 // Three launches on one stream, no atomics (deterministic):
-//   1. pre:  Delta for every row                         (memory bound)
+//   1. pre:  -Delta and -LSE log2(e) for every row       (memory bound)
 //   2. dkdv: one workgroup per key tile, walking its CSC column of query
 //            tiles; dK and dV stay in registers for the whole walk
 //   3. dq:   one workgroup per query tile, walking its CSR row of key tiles
+// The product kernels start each dP accumulation from -Delta, so the
+// products give dP - Delta, and take the exponent's row term ready-made.
 // Both product kernels stage 64-row chunks with direct global -> LDS copies
 // (row-major, XOR-swizzled; rows past N read as zeros, which contribute
 // exactly zero to every product here) and read transposed operands with the
@@ -29,12 +31,15 @@
 namespace radial {
 
 // ---------------------------------------------------------------------------
-// 1. Delta = rowsum(dO * O) in fp32
+// 1. -Delta = -rowsum(dO * O) in fp32, and the exponent's row term
+//    -LSE log2(e) (P = exp2(scale log2(e) S - LSE log2(e)))
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void radial_bwd_pre_kernel(const bf16 *__restrict__ O,
                                                              const bf16 *__restrict__ dO,
-                                                             float *__restrict__ delta,
+                                                             const float *__restrict__ lse,
+                                                             float *__restrict__ ndelta,
+                                                             float *__restrict__ nlse2,
                                                              int64_t rows) {
   constexpr int CH = D / 8;       // threads per row, 8 elements each
   constexpr int RPB = 256 / CH;   // rows per workgroup
@@ -50,7 +55,10 @@ __global__ __launch_bounds__(256) void radial_bwd_pre_kernel(const bf16 *__restr
   }
 #pragma unroll
   for (int off = CH / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-  if (row < rows && ch == 0) delta[row] = acc;
+  if (row < rows && ch == 0) {
+    ndelta[row] = -acc;
+    nlse2[row] = -lse[row] * kLog2e;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -110,8 +118,8 @@ struct BwdFlag {
 template <int D, int T, bool EXACT>
 __global__ __launch_bounds__(T / 32 * 64, 1) void radial_bwd_dkdv_kernel(
     const bf16 *__restrict__ Q, const bf16 *__restrict__ K, const bf16 *__restrict__ V,
-    const bf16 *__restrict__ dO, const float *__restrict__ LSE,
-    const float *__restrict__ Delta, bf16 *__restrict__ dK, bf16 *__restrict__ dV,
+    const bf16 *__restrict__ dO, const float *__restrict__ NLse2,
+    const float *__restrict__ NDelta, bf16 *__restrict__ dK, bf16 *__restrict__ dV,
     const int32_t *__restrict__ col_ptr, const int32_t *__restrict__ row_idx,
     const int32_t *__restrict__ col_order, int32_t N, int32_t nb, int32_t n_work,
     float scale_log2, float scale, MaskGeom mg) {
@@ -194,7 +202,7 @@ __global__ __launch_bounds__(T / 32 * 64, 1) void radial_bwd_dkdv_kernel(
     cp.copy_async(qd, (half ? dOb : Qb) + (int64_t)m0 * D, N - m0, wave);
     // row terms: wave w copies floats [w * 4 LPW, (w + 1) * 4 LPW) of each
     float *rd = lds_r + buf * 2 * C::MC + half * C::MC + wave * 4 * C::LPW;
-    const u32x4 rl = rsrc_words((half ? Delta : LSE) + rbase + m0, (N - m0) * 4);
+    const u32x4 rl = rsrc_words((half ? NDelta : NLse2) + rbase + m0, (N - m0) * 4);
     if (lane < C::LPW) dma16b_async(rl, rd, (wave * 4 * C::LPW + 4 * lane) * 4);
   };
   auto issue = [&](int c, int m0) __attribute__((always_inline)) {
@@ -213,8 +221,9 @@ __global__ __launch_bounds__(T / 32 * 64, 1) void radial_bwd_dkdv_kernel(
   // block j - 1 (b2, m2), stage 1 of block j (b1, m1), as flagged.  The step
   // is written as an explicit schedule of product slots (stage 3's products,
   // then stage 1's): slot i issues the LDS reads of slot i + RA, its own
-  // product and, from slot 4 on, a share of stage 2's elements (whose LSE and
-  // Delta terms are read in slots 0..3); a scheduling barrier after each slot
+  // product and, from slot 4 on, a share of stage 2's elements (whose LSE
+  // terms are read in slot 0; the -Delta terms that start stage 1's dP are
+  // read in slot 1, or 0 without stage 3); a scheduling barrier after each slot
   // keeps that order.  With one wave per SIMD, LDS latency is hidden only by
   // this read-ahead and the vector work only by this interleaving.
   auto step = [&](auto F1, auto F2, auto F3, int b1, int m1, int b2, int m2, int b3, int m3,
@@ -227,7 +236,8 @@ __global__ __launch_bounds__(T / 32 * 64, 1) void radial_bwd_dkdv_kernel(
     constexpr int RA = 4;                               // read-ahead (slots)
     const bf16 *Qs3 = lds_q + b3 * C::CHUNK, *dOs3 = lds_do + b3 * C::CHUNK;
     const bf16 *Qs1 = lds_q + b1 * C::CHUNK, *dOs1 = lds_do + b1 * C::CHUNK;
-    const float *rt2 = lds_r + b2 * 2 * C::MC + 32 * m2;
+    const float *rt2 = lds_r + b2 * 2 * C::MC + 32 * m2;           // -LSE log2(e), stage 2
+    const float *rt1 = lds_r + b1 * 2 * C::MC + C::MC + 32 * m1;   // -Delta, stage 1
     // operand of slot i: stage 3 slot -> (db, ks, dV or dK), stage 1 slot ->
     // (kk, S or dP)
     auto frag = [&](int i) __attribute__((always_inline)) {
@@ -246,14 +256,26 @@ __global__ __launch_bounds__(T / 32 * 64, 1) void radial_bwd_dkdv_kernel(
         else
           adk[db] = mfma32(a, pd_old[1][ks], adk[db]);
       } else {
+        // S starts from zero, dP from -Delta (read into it earlier), so
+        // stage 2 gets dP - Delta without a subtraction
         const int kk = (i - N3) / 2, w = (i - N3) % 2;
-        sd_new.sd[w] = kk == 0 ? mfma_v0(a, w ? vf[kk] : kf[kk])
-                               : mfma_v(a, w ? vf[kk] : kf[kk], sd_new.sd[w]);
+        sd_new.sd[w] = (kk == 0 && w == 0) ? mfma_v0(a, kf[kk])
+                                           : mfma_v(a, w ? vf[kk] : kf[kk], sd_new.sd[w]);
       }
     };
-    f32x4 rt[8];  // stage 2's LSE (0..3) and Delta (4..7) terms
+    f32x4 rt[4];  // stage 2's -LSE log2(e) terms
     auto rt_read = [&](int q) __attribute__((always_inline)) {
-      rt[q] = *reinterpret_cast<const f32x4 *>(&rt2[(q < 4 ? 0 : C::MC) + 8 * (q % 4) + 4 * g]);
+      rt[q] = *reinterpret_cast<const f32x4 *>(&rt2[8 * q + 4 * g]);
+    };
+    // stage 1's -Delta terms, straight into the dP accumulator (register r
+    // holds row 8 (r / 4) + 4 g + r % 4, as the terms' layout)
+    auto nd_read = [&]() __attribute__((always_inline)) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4 t = *reinterpret_cast<const f32x4 *>(&rt1[8 * q + 4 * g]);
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) sd_new.sd[1][4 * q + jj] = t[jj];
+      }
     };
     // stage 2, element pair e (rows r = 2e, 2e + 1 of the block)
     auto stage2_pair = [&](int e) __attribute__((always_inline)) {
@@ -263,9 +285,9 @@ __global__ __launch_bounds__(T / 32 * 64, 1) void radial_bwd_dkdv_kernel(
         float sv = sd_old.sd[0][r];
         // token-exact: okm holds the stage-2 block's allowed rows (bit r)
         if constexpr (EXACT) sv = ((okm >> r) & 1u) ? sv : -INFINITY;
-        const float p = fast_exp2(fmaf(sv, scale_log2, -rt[i][jj] * kLog2e));
+        const float p = fast_exp2(fmaf(sv, scale_log2, rt[i][jj]));
         pd_new[0][r >> 3][r & 7] = bf16(p);
-        pd_new[1][r >> 3][r & 7] = bf16(p * (sd_old.sd[1][r] - rt[4 + i][jj]));
+        pd_new[1][r >> 3][r & 7] = bf16(p * sd_old.sd[1][r]);
       }
     };
     // stage 2 runs alongside stage 3's products when there are any (so the
@@ -279,10 +301,14 @@ __global__ __launch_bounds__(T / 32 * 64, 1) void radial_bwd_dkdv_kernel(
 #pragma unroll
     for (int i = 0; i < NSL; ++i) {
       if constexpr (s2) {
-        if (i < 2) {
+        if (i == 0) {
 #pragma unroll
-          for (int q = 4 * i; q < 4 * i + 4; ++q) rt_read(q);
+          for (int q = 0; q < 4; ++q) rt_read(q);
         }
+      }
+      // the -Delta terms land before the first dP product (slot N3 + 1)
+      if constexpr (s1) {
+        if (i == (N3 > 0 ? 1 : 0)) nd_read();
       }
       if (i + RA < NSL) fr[i + RA] = frag(i + RA);
       product(i, fr[i]);
@@ -298,7 +324,7 @@ __global__ __launch_bounds__(T / 32 * 64, 1) void radial_bwd_dkdv_kernel(
     }
     if constexpr (s2 && SEND <= S0) {
 #pragma unroll
-      for (int q = 0; q < 8; ++q) rt_read(q);
+      for (int q = 0; q < 4; ++q) rt_read(q);
 #pragma unroll
       for (int e = 0; e < 8; ++e) stage2_pair(e);
     }
@@ -425,8 +451,8 @@ struct DqCfg {
 template <int D, int T, bool EXACT>
 __global__ __launch_bounds__(T / 32 * 64, 2) void radial_bwd_dq_kernel(
     const bf16 *__restrict__ Q, const bf16 *__restrict__ K, const bf16 *__restrict__ V,
-    const bf16 *__restrict__ dO, const float *__restrict__ LSE,
-    const float *__restrict__ Delta, bf16 *__restrict__ dQ,
+    const bf16 *__restrict__ dO, const float *__restrict__ NLse2,
+    const float *__restrict__ NDelta, bf16 *__restrict__ dQ,
     const int32_t *__restrict__ row_ptr, const int32_t *__restrict__ col_idx, int32_t N,
     int32_t nb, int32_t n_work, float scale_log2, float scale, MaskGeom mg) {
   using C = DqCfg<D, T>;
@@ -450,9 +476,9 @@ __global__ __launch_bounds__(T / 32 * 64, 2) void radial_bwd_dq_kernel(
     qf[kk] = q_ok ? ld8(Q + base + (int64_t)qrow * D + kk * 16 + g * 8) : zero_bf16x8();
     dof[kk] = q_ok ? ld8(dO + base + (int64_t)qrow * D + kk * 16 + g * 8) : zero_bf16x8();
   }
-  // rows past N: Q, dO are zero and LSE, Delta are taken as 0, so dS = 0
-  const float lse2 = q_ok ? LSE[(int64_t)bh * N + qrow] * kLog2e : 0.f;
-  const float dl = q_ok ? Delta[(int64_t)bh * N + qrow] : 0.f;
+  // rows past N: Q, dO are zero and the row terms are taken as 0, so dS = 0
+  const float nl2 = q_ok ? NLse2[(int64_t)bh * N + qrow] : 0.f;   // -LSE log2(e)
+  const float ndl = q_ok ? NDelta[(int64_t)bh * N + qrow] : 0.f;  // -Delta
 
   f32x16 adq[C::NDB];
 #pragma unroll
@@ -512,7 +538,10 @@ __global__ __launch_bounds__(T / 32 * 64, 2) void radial_bwd_dq_kernel(
         ka[kk] = ld8(Ks + swz<D>(kb * 32 + c32, 2 * kk + g));
         va[kk] = ld8(Vs + swz<D>(kb * 32 + c32, 2 * kk + g));
       }
-      f32x16 s = zero16(), dp = zero16();
+      // dP starts from -Delta, so the products give dP - Delta directly
+      f32x16 s = zero16(), dp;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dp[r] = ndl;
 #pragma unroll
       for (int kk = 0; kk < C::NKK; ++kk) {
         s = mfma32(ka[kk], qf[kk], s);
@@ -527,8 +556,8 @@ __global__ __launch_bounds__(T / 32 * 64, 2) void radial_bwd_dq_kernel(
       bf16x8 dsb[2];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p = fast_exp2(fmaf(s[r], scale_log2, -lse2));
-        dsb[r >> 3][r & 7] = bf16(p * (dp[r] - dl));
+        const float p = fast_exp2(fmaf(s[r], scale_log2, nl2));
+        dsb[r >> 3][r & 7] = bf16(p * dp[r]);
       }
 #pragma unroll
       for (int db = 0; db < C::NDB; ++db)
@@ -564,22 +593,22 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t stream) {
   const int64_t rows = (int64_t)a.BH * a.N;
   constexpr int RPB = 256 / (D / 8);
   hipLaunchKernelGGL((radial_bwd_pre_kernel<D>), dim3((unsigned)((rows + RPB - 1) / RPB)),
-                     dim3(256), 0, stream, (const bf16 *)a.o, (const bf16 *)a.dout, a.delta,
-                     rows);
+                     dim3(256), 0, stream, (const bf16 *)a.o, (const bf16 *)a.dout, a.lse,
+                     a.ndelta, a.nlse2, rows);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t works = (int64_t)a.BH * a.nb;
   const float sl2 = a.scale * kLog2e;
   hipLaunchKernelGGL((radial_bwd_dkdv_kernel<D, T, EXACT>), dim3((unsigned)works),
                      dim3(DkdvCfg<D, T>::NT), 0, stream, (const bf16 *)a.q, (const bf16 *)a.k,
-                     (const bf16 *)a.v, (const bf16 *)a.dout, a.lse, a.delta, (bf16 *)a.dk,
+                     (const bf16 *)a.v, (const bf16 *)a.dout, a.nlse2, a.ndelta, (bf16 *)a.dk,
                      (bf16 *)a.dv, a.col_ptr, a.row_idx, a.col_order, a.N, a.nb, (int32_t)works,
                      sl2, a.scale, a.mask);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((radial_bwd_dq_kernel<D, T, EXACT>), dim3((unsigned)works),
                      dim3(DqCfg<D, T>::NT), 0, stream, (const bf16 *)a.q, (const bf16 *)a.k,
-                     (const bf16 *)a.v, (const bf16 *)a.dout, a.lse, a.delta, (bf16 *)a.dq,
+                     (const bf16 *)a.v, (const bf16 *)a.dout, a.nlse2, a.ndelta, (bf16 *)a.dq,
                      a.row_ptr, a.col_idx, a.N, a.nb, (int32_t)works, sl2, a.scale, a.mask);
   return hipGetLastError();
 }

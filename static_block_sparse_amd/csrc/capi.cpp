@@ -298,8 +298,9 @@ size_t radial_attn_bwd_workspace_bytes(const radial_layout *L, int32_t B, int32_
   (void)L;
   (void)D;
   if (B < 1 || H < 1 || N < 1) return 0;
+  // two fp32 row arrays: -Delta and -LSE * log2(e), each 256-byte aligned
   const size_t bytes = (size_t)B * (size_t)H * (size_t)N * sizeof(float);
-  return (bytes + 255) & ~size_t(255);
+  return 2 * ((bytes + 255) & ~size_t(255));
 }
 
 int radial_attn_bwd(const radial_layout *L, int32_t B, int32_t H, int64_t N, int32_t D,
@@ -333,7 +334,8 @@ int radial_attn_bwd(const radial_layout *L, int32_t B, int32_t H, int64_t N, int
   a.dq = dq;
   a.dk = dk;
   a.dv = dv;
-  a.delta = static_cast<float *>(workspace);
+  a.ndelta = static_cast<float *>(workspace);
+  a.nlse2 = reinterpret_cast<float *>(static_cast<char *>(workspace) + need / 2);
   a.row_ptr = L->d_row_ptr;
   a.col_idx = L->d_col_idx;
   a.col_ptr = L->d_col_ptr;

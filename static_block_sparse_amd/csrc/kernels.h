@@ -40,7 +40,8 @@ struct BwdArgs {
   const void *q, *k, *v, *o, *dout;
   const float *lse;
   void *dq, *dk, *dv;
-  float *delta;                      // workspace, fp32 [BH, N]
+  float *ndelta;                     // workspace: -rowsum(dO * O), fp32 [BH, N]
+  float *nlse2;                      // workspace: -LSE * log2(e), fp32 [BH, N]
   const int32_t *row_ptr, *col_idx;  // CSR (dQ pass)
   const int32_t *col_ptr, *row_idx;  // CSC (dK/dV pass)
   const int32_t *col_order;          // key tiles, longest column first
