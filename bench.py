@@ -232,6 +232,7 @@ def main():
                        "kept_pairs_per_head": L.nnz_pairs},
             "fwd_latency_ms": round(ms, 4),
             "fwd_latency_min_ms": round(min(per), 4),
+            "fwd_latency_median_ms": round(float(np.median(per)), 4),
             "roofline": {"bound": "mfma", "kernel": "radial_fwd_kernel<128,128>",
                          "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
@@ -349,8 +350,11 @@ def main():
     if not args.no_cpu_baseline:
         from oracle import mask as om
         log("cpu baseline (oracle) ...")
+        t = time.perf_counter()
         kept = om.kept_tiles(w.frames, w.tokens_per_frame, w.T, True)
+        oracle_mask_s = time.perf_counter() - t
         result["cpu_baseline"] = cpu_baseline(w, kept)
+        result["cpu_baseline"]["oracle_mask_build_s"] = round(oracle_mask_s, 3)
         log("cpu baseline:", result["cpu_baseline"]["sample"])
     else:
         result["cpu_baseline"] = None

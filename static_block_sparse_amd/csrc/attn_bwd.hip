@@ -210,6 +210,26 @@ __global__ __launch_bounds__(T / 32 * 64, 1) void radial_bwd_dkdv_kernel(
     issue_half(c, m0, 1);
   };
 
+  // Per-lane LDS offsets of the operand reads, the same for every chunk
+  // buffer, block half and k step: the swizzle term of a row depends on the
+  // row modulo 16 only, and blocks start at multiples of 16 rows.
+  //   soff[kk]: stage 1, row c32, 16-byte column block 2 kk + g (ld8)
+  //   toff[db][h]: stage 3, the transposing reads of ld_trA for column block
+  //                db, rows r and r + 8 of the first 16-row step
+  int soff[C::NKK], toff[C::NDB][2];
+#pragma unroll
+  for (int kk = 0; kk < C::NKK; ++kk) soff[kk] = swz<D>(c32, 2 * kk + g);
+  {
+    const int j = lane & 15, G = lane >> 4;
+    const int r0 = 4 * (G >> 1) + (j >> 2);
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db) {
+      const int col = db * 32 + 16 * (G & 1) + 4 * (j & 3);
+      toff[db][0] = swz<D>(r0, col >> 3) + (col & 7);
+      toff[db][1] = swz<D>(r0 + 8, col >> 3) + (col & 7);
+    }
+  }
+
   // stage-1 results of a block: sd[0] = S, sd[1] = dP (register r holds
   // query row 32 mb + 8 (r / 4) + 4 g + r % 4 of the chunk, for key column
   // c32)
@@ -240,13 +260,15 @@ __global__ __launch_bounds__(T / 32 * 64, 1) void radial_bwd_dkdv_kernel(
     const float *rt1 = lds_r + b1 * 2 * C::MC + C::MC + 32 * m1;   // -Delta, stage 1
     // operand of slot i: stage 3 slot -> (db, ks, dV or dK), stage 1 slot ->
     // (kk, S or dP)
+    // (lane offsets precomputed; the block's row offset is a constant)
     auto frag = [&](int i) __attribute__((always_inline)) {
       if (i < N3) {
         const int db = i / 4, ks = (i / 2) % 2;
-        return ld_trA<D>(i % 2 ? Qs3 : dOs3, db, m3, ks, lane);
+        const bf16 *t = (i % 2 ? Qs3 : dOs3) + (m3 * 32 + ks * 16) * D;
+        return cat(ld_tr(t + toff[db][0]), ld_tr(t + toff[db][1]));
       }
       const int kk = (i - N3) / 2;
-      return ld8((((i - N3) % 2) ? dOs1 : Qs1) + swz<D>(m1 * 32 + c32, 2 * kk + g));
+      return ld8((((i - N3) % 2) ? dOs1 : Qs1) + m1 * 32 * D + soff[kk]);
     };
     auto product = [&](int i, bf16x8 a) __attribute__((always_inline)) {
       if (i < N3) {
