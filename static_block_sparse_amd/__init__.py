@@ -262,6 +262,11 @@ def attn_fwd(q, k, v, layout: Layout, scale: float | None = None, out=None, lse=
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     o = torch.empty_like(q) if out is None else out
     l = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    if out is not None:
+        _check_qkv("out", o, q)
+    if lse is not None and (l.dtype != torch.float32 or tuple(l.shape) != (B, H, N)
+                            or not l.is_contiguous() or l.device != q.device):
+        raise ValueError("lse must be contiguous fp32 [B, H, N] on q's device")
     layout.upload(q.device)
     with torch.cuda.device(q.device):
         stream = torch.cuda.current_stream(q.device).cuda_stream
@@ -271,8 +276,9 @@ def attn_fwd(q, k, v, layout: Layout, scale: float | None = None, out=None, lse=
 
 
 def attn_bwd(q, k, v, o, lse, do, layout: Layout, scale: float | None = None,
-             workspace=None):
-    """Radial attention backward.  Returns (dq, dk, dv), bf16 [B,H,N,D]."""
+             workspace=None, out=None):
+    """Radial attention backward.  Returns (dq, dk, dv), bf16 [B,H,N,D].
+    ``out``: optional (dq, dk, dv) tensors to write into."""
     import torch
     for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
         _check_qkv(name, t, None if name == "q" else q)
@@ -280,7 +286,12 @@ def attn_bwd(q, k, v, o, lse, do, layout: Layout, scale: float | None = None,
     if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N) or not lse.is_contiguous():
         raise ValueError("lse must be contiguous fp32 [B, H, N]")
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    if out is None:
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    else:
+        dq, dk, dv = out
+        for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+            _check_qkv(name, t, q)
     need = lib().radial_attn_bwd_workspace_bytes(layout.handle, B, H, N, D)
     ws = workspace
     if ws is None or ws.numel() * ws.element_size() < need:

@@ -1,0 +1,126 @@
+// Test infrastructure: a host-memory stand-in for the HIP runtime and the
+// kernel launchers, linked with the library's host sources (mask compiler and
+// C ABI) into an AddressSanitizer / UndefinedBehaviorSanitizer build.
+//
+// Device allocations are plain heap blocks, so the sanitizers see every
+// layout copy the C ABI makes.  The launchers run no kernel: they check the
+// arguments the C ABI assembled and read or write the first and last element
+// of every range a kernel would touch (inputs read, outputs and workspace
+// written), so a wrong size or offset shows up as a heap overflow.
+#include <hip/hip_runtime_api.h>
+
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
+#include "kernels.h"
+
+namespace {
+
+int g_fail = 0;
+
+void check(bool ok, const char *what) {
+  if (!ok) {
+    std::fprintf(stderr, "fake device: check failed: %s\n", what);
+    g_fail = 1;
+  }
+}
+
+// volatile accesses so the compiler keeps them
+void read_range(const void *p, size_t bytes) {
+  if (!bytes) return;
+  const volatile unsigned char *c = static_cast<const volatile unsigned char *>(p);
+  (void)c[0];
+  (void)c[bytes - 1];
+}
+void write_range(void *p, size_t bytes) {
+  if (!bytes) return;
+  volatile unsigned char *c = static_cast<volatile unsigned char *>(p);
+  c[0] = 0;
+  c[bytes - 1] = 0;
+}
+
+// tile lists: row_ptr (nb + 1) and its index list, indices below nb once bit
+// 31 (the partial-tile mark) is cleared
+void check_lists(const int32_t *ptr, const int32_t *idx, int32_t nb, const char *what) {
+  check(ptr[0] == 0, what);
+  for (int32_t u = 0; u < nb; ++u) check(ptr[u + 1] >= ptr[u], what);
+  for (int32_t t = 0; t < ptr[nb]; ++t) {
+    const int32_t v = idx[t] & 0x7fffffff;
+    check(v >= 0 && v < nb, what);
+  }
+}
+
+void check_mask(const radial::MaskGeom &m) {
+  check(m.s >= 1 && m.frames >= 1, "mask geometry");
+  check(m.band_rtab != nullptr, "band table uploaded");
+  read_range(m.band_rtab, 64 * sizeof(int32_t));
+  check(m.s_shift >= 31 && m.s_shift <= 62, "division shift");
+}
+
+}  // namespace
+
+extern "C" int fake_device_failures() { return g_fail; }
+
+// ---- HIP runtime entry points the C ABI uses --------------------------------
+hipError_t hipGetDevice(int *device) {
+  if (std::getenv("FAKE_DEVICE_NONE")) return hipErrorNoDevice;
+  *device = 0;
+  return hipSuccess;
+}
+hipError_t hipSetDevice(int) { return hipSuccess; }
+hipError_t hipMalloc(void **ptr, size_t size) {
+  *ptr = std::malloc(size ? size : 1);
+  return *ptr ? hipSuccess : hipErrorOutOfMemory;
+}
+hipError_t hipFree(void *ptr) {
+  std::free(ptr);
+  return hipSuccess;
+}
+hipError_t hipMemcpy(void *dst, const void *src, size_t bytes, hipMemcpyKind) {
+  std::memcpy(dst, src, bytes);
+  return hipSuccess;
+}
+hipError_t hipGetLastError(void) { return hipSuccess; }
+const char *hipGetErrorString(hipError_t) { return "fake device error"; }
+
+// ---- kernel launchers ---------------------------------------------------------
+namespace radial {
+
+hipError_t launch_fwd(const FwdArgs &a, hipStream_t) {
+  const size_t x = size_t(a.BH) * a.N * a.D * 2, r = size_t(a.BH) * a.N * 4;
+  check(a.BH >= 1 && a.N >= 1 && a.nb == (a.N + a.T - 1) / a.T, "forward sizes");
+  read_range(a.q, x);
+  read_range(a.k, x);
+  read_range(a.v, x);
+  write_range(a.o, x);
+  write_range(a.lse, r);
+  check_lists(a.row_ptr, a.col_idx, a.nb, "forward CSR");
+  check_mask(a.mask);
+  return hipSuccess;
+}
+
+hipError_t launch_bwd(const BwdArgs &a, hipStream_t) {
+  const size_t x = size_t(a.BH) * a.N * a.D * 2, r = size_t(a.BH) * a.N * 4;
+  check(a.BH >= 1 && a.N >= 1 && a.nb == (a.N + a.T - 1) / a.T, "backward sizes");
+  for (const void *p : {a.q, a.k, a.v, a.o, a.dout}) read_range(p, x);
+  read_range(a.lse, r);
+  for (void *p : {a.dq, a.dk, a.dv}) write_range(p, x);
+  write_range(a.ndelta, r);
+  write_range(a.nlse2, r);
+  check(a.nlse2 >= a.ndelta + size_t(a.BH) * a.N, "workspace arrays overlap");
+  check_lists(a.row_ptr, a.col_idx, a.nb, "backward CSR");
+  check_lists(a.col_ptr, a.row_idx, a.nb, "backward CSC");
+  // col_order: a permutation of the key tiles
+  unsigned char *seen = static_cast<unsigned char *>(std::calloc(a.nb, 1));
+  for (int32_t i = 0; i < a.nb; ++i) {
+    const int32_t v = a.col_order[i];
+    check(v >= 0 && v < a.nb && !seen[v], "column order is a permutation");
+    if (v >= 0 && v < a.nb) seen[v] = 1;
+  }
+  std::free(seen);
+  check_mask(a.mask);
+  return hipSuccess;
+}
+
+}  // namespace radial
