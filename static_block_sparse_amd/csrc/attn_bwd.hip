@@ -258,13 +258,15 @@ __global__ __launch_bounds__(T / 32 * 64, 1) void radial_bwd_dkdv_kernel(
     const bf16 *Qs1 = lds_q + b1 * C::CHUNK, *dOs1 = lds_do + b1 * C::CHUNK;
     const float *rt2 = lds_r + b2 * 2 * C::MC + 32 * m2;           // -LSE log2(e), stage 2
     const float *rt1 = lds_r + b1 * 2 * C::MC + C::MC + 32 * m1;   // -Delta, stage 1
-    // operand of slot i: stage 3 slot -> (db, ks, dV or dK), stage 1 slot ->
-    // (kk, S or dP)
-    // (lane offsets precomputed; the block's row offset is a constant)
+    // operand of slot i (lane offsets precomputed; the block's row offset is
+    // a constant).  Stage 3 slot i: k step ks = i / (2 NDB), dV (w = 0) or
+    // dK (w = 1) by (i / NDB) % 2, column block db = i % NDB, so runs of NDB
+    // consecutive products share their P or dS operand (less switching).
+    // Stage 1 slot: (kk, S or dP).
     auto frag = [&](int i) __attribute__((always_inline)) {
       if (i < N3) {
-        const int db = i / 4, ks = (i / 2) % 2;
-        const bf16 *t = (i % 2 ? Qs3 : dOs3) + (m3 * 32 + ks * 16) * D;
+        const int db = i % C::NDB, ks = i / (2 * C::NDB), w = (i / C::NDB) % 2;
+        const bf16 *t = (w ? Qs3 : dOs3) + (m3 * 32 + ks * 16) * D;
         return cat(ld_tr(t + toff[db][0]), ld_tr(t + toff[db][1]));
       }
       const int kk = (i - N3) / 2;
@@ -272,8 +274,8 @@ __global__ __launch_bounds__(T / 32 * 64, 1) void radial_bwd_dkdv_kernel(
     };
     auto product = [&](int i, bf16x8 a) __attribute__((always_inline)) {
       if (i < N3) {
-        const int db = i / 4, ks = (i / 2) % 2;
-        if (i % 2 == 0)
+        const int db = i % C::NDB, ks = i / (2 * C::NDB), w = (i / C::NDB) % 2;
+        if (w == 0)
           adv[db] = mfma32(a, pd_old[0][ks], adv[db]);
         else
           adk[db] = mfma32(a, pd_old[1][ks], adk[db]);
@@ -581,10 +583,11 @@ __global__ __launch_bounds__(T / 32 * 64, 2) void radial_bwd_dq_kernel(
         const float p = fast_exp2(fmaf(s[r], scale_log2, nl2));
         dsb[r >> 3][r & 7] = bf16(p * dp[r]);
       }
+      // consecutive products share their dS operand (less switching)
 #pragma unroll
-      for (int db = 0; db < C::NDB; ++db)
+      for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
+        for (int db = 0; db < C::NDB; ++db)
           adq[db] = mfma32(ld_trA<D>(Ks, db, kb, ks, lane), dsb[ks], adq[db]);
     }
 

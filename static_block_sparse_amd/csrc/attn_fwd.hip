@@ -165,15 +165,15 @@ __global__ __launch_bounds__(T / 32 * 64, 2) void radial_fwd_kernel(
     f32x16 s[C::NKB];
     bf16x8 kf[C::NKB][C::NKK];
 #pragma unroll
-    for (int kb = 0; kb < C::NKB; ++kb)
+    for (int kk = 0; kk < C::NKK; ++kk)
 #pragma unroll
-      for (int kk = 0; kk < C::NKK; ++kk) kf[kb][kk] = ld8(Ks + swz<D>(kb * 32 + c32, 2 * kk + g));
+      for (int kb = 0; kb < C::NKB; ++kb) kf[kb][kk] = ld8(Ks + swz<D>(kb * 32 + c32, 2 * kk + g));
 #pragma unroll
-    for (int kb = 0; kb < C::NKB; ++kb) {
-      s[kb] = zero16();
+    for (int kb = 0; kb < C::NKB; ++kb) s[kb] = zero16();
 #pragma unroll
-      for (int kk = 0; kk < C::NKK; ++kk) s[kb] = mfma32(kf[kb][kk], qf[kk], s[kb]);
-    }
+    for (int kk = 0; kk < C::NKK; ++kk)
+#pragma unroll
+      for (int kb = 0; kb < C::NKB; ++kb) s[kb] = mfma32(kf[kb][kk], qf[kk], s[kb]);
     __builtin_amdgcn_sched_group_barrier(0x100, C::NKK, 1);  // block 0 reads
 #pragma unroll
     for (int i = 0; i < C::NKK * (C::NKB - 1); ++i) {
@@ -232,12 +232,12 @@ __global__ __launch_bounds__(T / 32 * 64, 2) void radial_fwd_kernel(
 
     // O^T += V^T P^T
 #pragma unroll
-    for (int db = 0; db < C::NDB; ++db) {
-      const int col = db * 32 + 16 * (G & 1) + 4 * (j & 3);
+    for (int kb = 0; kb < C::NKB; ++kb) {
 #pragma unroll
-      for (int kb = 0; kb < C::NKB; ++kb) {
+      for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
+        for (int db = 0; db < C::NDB; ++db) {
+          const int col = db * 32 + 16 * (G & 1) + 4 * (j & 3);
           const int n0 = kb * 32 + ks * 16 + 4 * (G >> 1) + (j >> 2);
           const bf16x4 lo = ld_tr(Vs + swz<D>(n0, col >> 3) + (col & 7));
           const bf16x4 hi = ld_tr(Vs + swz<D>(n0 + 8, col >> 3) + (col & 7));
