@@ -236,7 +236,7 @@ def main():
             "roofline": {"bound": "mfma", "kernel": "radial_fwd_kernel<128,128>",
                          "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                         "traffic": traffic,
+                         "traffic": traffic, "traffic_unit": "bytes per launch (HBM side)",
                          "alg_flops_per_launch": fwd_flops, "avg_launch_ms": round(launch_ms, 4)},
             "mask_build_ms": round(build_ms, 2),
         }
