@@ -28,6 +28,13 @@
 //  * the running max is only moved when a chunk's max exceeds it by more
 //    than 8 (log2 units); probabilities then stay below 2^8, exact in the
 //    final O / l and LSE, and the O rescale is skipped on most chunks.
+//  * pairs (PAIR, the default): a workgroup of 2 T / 32 waves takes the
+//    adjacent query tiles 2p and 2p + 1 and walks the sorted union of their
+//    key tiles (built by the mask compiler).  Every staged chunk then serves
+//    both tiles' waves, which halves the global -> LDS copies per product;
+//    at the power cap the copies' energy is a large share of the budget.
+//    A wave skips the chunks of key tiles its own tile does not keep (5-15%
+//    of the walk for the radial mask).
 //  * token-exact layouts (EXACT): in the chunks of tiles marked partial,
 //    each lane masks the keys outside its query's allowed runs (one per key
 //    frame the chunk touches, however many) before the max.
@@ -36,15 +43,19 @@
 #include "device_common.h"
 #include "kernels.h"
 
+#ifndef RADIAL_FWD_PAIR
+#define RADIAL_FWD_PAIR 1  // query tiles processed in pairs sharing K/V chunks
+#endif
 #ifndef RADIAL_FWD_XCD_BLOCK
-#define RADIAL_FWD_XCD_BLOCK 16  // query tiles per XCD block (see xcd_remap)
+#define RADIAL_FWD_XCD_BLOCK 16  // work items per XCD block (see xcd_remap)
 #endif
 
 namespace radial {
 
-template <int D, int T>
+template <int D, int T, bool PAIR>
 struct FwdCfg {
-  static constexpr int NW = T / 32;     // waves per workgroup
+  static constexpr int NWR = T / 32;    // waves per query tile
+  static constexpr int NW = NWR * (PAIR ? 2 : 1);  // waves per workgroup
   static constexpr int NT = NW * 64;    // threads per workgroup
   static constexpr int KC = 64;         // keys per pipeline chunk
   static constexpr int CPT = T / KC;    // chunks per tile
@@ -57,28 +68,36 @@ struct FwdCfg {
   static_assert(NDMA >= 1 && CHUNK * 2 % (1024 * NW) == 0, "chunk must split evenly");
 };
 
-template <int D, int T, bool EXACT>
-__global__ __launch_bounds__(T / 32 * 64, 2) void radial_fwd_kernel(
+template <int D, int T, bool EXACT, bool PAIR>
+__global__ __launch_bounds__(T / 32 * 64 * (PAIR ? 2 : 1),
+                             PAIR ? 256 / (T / 32 * 64) : 2) void radial_fwd_kernel(
     const bf16 *__restrict__ Q, const bf16 *__restrict__ K, const bf16 *__restrict__ V,
     bf16 *__restrict__ O, float *__restrict__ LSE, const int32_t *__restrict__ row_ptr,
-    const int32_t *__restrict__ col_idx, int32_t N, int32_t nb, int32_t n_work,
+    const int32_t *__restrict__ col_idx, const int32_t *__restrict__ pair_ptr,
+    const int32_t *__restrict__ pair_idx, int32_t N, int32_t nb, int32_t n_work,
     float scale_log2, MaskGeom mg) {
-  using C = FwdCfg<D, T>;
+  using C = FwdCfg<D, T, PAIR>;
   constexpr float kSlack = 8.f;  // lazy-rescale threshold (log2 units)
   __shared__ __attribute__((aligned(1024))) bf16 lds[2 * C::BUF];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c32 = lane & 31, g = lane >> 5;
+  // work item: one query tile, or with PAIR the query tiles 2p (waves
+  // [0, NWR)) and 2p + 1 (waves [NWR, 2 NWR)) over the union of their key
+  // tiles, so every staged K/V chunk serves twice the queries
+  const int nwork_head = PAIR ? (nb + 1) / 2 : nb;
   const int work = xcd_remap(blockIdx.x, n_work, RADIAL_FWD_XCD_BLOCK);
-  const int bh = work / nb;
-  const int u = work - bh * nb;
+  const int bh = work / nwork_head;
+  const int wi = work - bh * nwork_head;
+  const int sub = PAIR ? wave / C::NWR : 0;  // which tile of the pair
+  const int u = PAIR ? 2 * wi + sub : wi;
   const int64_t base = (int64_t)bh * N * D;
   const bf16 *Kb = K + base;
   const bf16 *Vb = V + base;
 
-  const int qrow = u * T + wave * 32 + c32;
-  const bool q_ok = qrow < N;
+  const int qrow = u * T + (wave % C::NWR) * 32 + c32;
+  const bool q_ok = u < nb && qrow < N;
   // token-exact: the mask's per-band table, read by the predicate from LDS
   __shared__ int lds_rtab[64];
   int rtab_v = 0;
@@ -88,19 +107,21 @@ __global__ __launch_bounds__(T / 32 * 64, 2) void radial_fwd_kernel(
   for (int kk = 0; kk < C::NKK; ++kk)
     qf[kk] = q_ok ? ld8(Q + base + (int64_t)qrow * D + kk * 16 + g * 8) : zero_bf16x8();
 
-  // chunk list: every KC-key chunk of every kept tile, minus the chunks of
-  // the last key tile that lie entirely at or beyond N
-  const int t_begin = row_ptr[u], t_end = row_ptr[u + 1];
+  // chunk list: every KC-key chunk of every listed key tile, minus the
+  // chunks of the last key tile that lie entirely at or beyond N.  A list
+  // entry is a key tile (CSR: bit 31 marks a partial tile; pair lists:
+  // membership and partial bits per tile of the pair, see kernels.h).
+  const int32_t *lptr = PAIR ? pair_ptr : row_ptr;
+  const int32_t *lidx = PAIR ? pair_idx : col_idx;
+  constexpr int32_t TMASK = PAIR ? kPairTile : 0x7fffffff;
+  const int t_begin = lptr[wi], t_end = lptr[wi + 1];
   int nchunks = (t_end - t_begin) * C::CPT;
-  if (t_end > t_begin && (col_idx[t_end - 1] & 0x7fffffff) == nb - 1)
+  if (t_end > t_begin && (lidx[t_end - 1] & TMASK) == nb - 1)
     nchunks -= C::CPT - (N - (nb - 1) * T + C::KC - 1) / C::KC;
-  // first key of chunk c, with bit 31 set when its tile is marked partial:
-  // scalar loads, fetched one chunk ahead so their wait lands where no LDS
-  // or vector-memory work is outstanding
-  auto chunk_key0 = [&](int c) {
-    const int raw = col_idx[t_begin + c / C::CPT];
-    return ((raw & 0x7fffffff) * T + (c % C::CPT) * C::KC) | (raw & int(0x80000000));
-  };
+  // list entry of chunk c: scalar loads, fetched one chunk ahead so their
+  // wait lands where no LDS or vector-memory work is outstanding
+  auto chunk_raw = [&](int c) { return lidx[t_begin + c / C::CPT]; };
+  auto key_of = [&](int raw, int c) { return (raw & TMASK) * T + (c % C::CPT) * C::KC; };
   // this lane's query as (frame, position), for the token predicate
   const int qi = qrow / mg.s, qa = qrow - (qrow / mg.s) * mg.s;
 
@@ -135,9 +156,9 @@ __global__ __launch_bounds__(T / 32 * 64, 2) void radial_fwd_kernel(
   float m_run = kNoMax;     // reference max of the log2-scaled logits
   float l_run = 0.f;        // this lane's share of the running sum
 
-  int key_next = nchunks > 0 ? chunk_key0(0) : 0;            // chunk c + 1
-  int key_after = nchunks > 1 ? chunk_key0(1) : 0;           // chunk c + 2
-  if (nchunks > 0) issue_copy(0, key_next & 0x7fffffff);
+  int raw_next = nchunks > 0 ? chunk_raw(0) : 0;             // chunk c + 1
+  int raw_after = nchunks > 1 ? chunk_raw(1) : 0;            // chunk c + 2
+  if (nchunks > 0) issue_copy(0, key_of(raw_next, 0));
   wait_vmem();  // Q fragments and the first chunk
   if constexpr (EXACT) {
     if (tid < 64) lds_rtab[tid] = rtab_v;
@@ -152,108 +173,114 @@ __global__ __launch_bounds__(T / 32 * 64, 2) void radial_fwd_kernel(
   for (int c = 0; c < nchunks; ++c) {
     const bf16 *Ks = lds + (c & 1) * C::BUF;
     const bf16 *Vs = Ks + C::KC * D;
-    const int key0 = key_next & 0x7fffffff;
-    const bool partial = EXACT && key_next < 0;
-    key_next = key_after;
+    const int raw = raw_next;
+    const int key0 = key_of(raw, c);
+    // this wave's tile takes part in the chunk (always without PAIR)
+    const bool member = PAIR ? ((raw >> (27 + sub)) & 1) != 0 : true;
+    const bool partial = EXACT && (PAIR ? ((raw >> (29 + sub)) & 1) != 0 : raw < 0);
+    raw_next = raw_after;
     // the next chunk's copy lands in the other buffer during these products
-    if (c + 1 < nchunks) issue_copy((c + 1) & 1, key_next & 0x7fffffff);
-    if (c + 2 < nchunks) key_after = chunk_key0(c + 2);
+    if (c + 1 < nchunks) issue_copy((c + 1) & 1, key_of(raw_next, c + 1));
+    if (c + 2 < nchunks) raw_after = chunk_raw(c + 2);
 
-    // S^T for the wave's 32 queries against the chunk's KC keys.  The K
-    // fragments of block kb + 1 are read while block kb's products run, so
-    // the LDS latency is paid once per chunk rather than once per product.
-    f32x16 s[C::NKB];
-    bf16x8 kf[C::NKB][C::NKK];
+    if (member) {
+      // S^T for the wave's 32 queries against the chunk's KC keys.  The K
+      // fragments of block kb + 1 are read while block kb's products run, so
+      // the LDS latency is paid once per chunk rather than once per product.
+      f32x16 s[C::NKB];
+      bf16x8 kf[C::NKB][C::NKK];
 #pragma unroll
-    for (int kk = 0; kk < C::NKK; ++kk)
+      for (int kk = 0; kk < C::NKK; ++kk)
 #pragma unroll
-      for (int kb = 0; kb < C::NKB; ++kb) kf[kb][kk] = ld8(Ks + swz<D>(kb * 32 + c32, 2 * kk + g));
+        for (int kb = 0; kb < C::NKB; ++kb)
+          kf[kb][kk] = ld8(Ks + swz<D>(kb * 32 + c32, 2 * kk + g));
 #pragma unroll
-    for (int kb = 0; kb < C::NKB; ++kb) s[kb] = zero16();
+      for (int kb = 0; kb < C::NKB; ++kb) s[kb] = zero16();
 #pragma unroll
-    for (int kk = 0; kk < C::NKK; ++kk)
+      for (int kk = 0; kk < C::NKK; ++kk)
 #pragma unroll
-      for (int kb = 0; kb < C::NKB; ++kb) s[kb] = mfma32(kf[kb][kk], qf[kk], s[kb]);
-    __builtin_amdgcn_sched_group_barrier(0x100, C::NKK, 1);  // block 0 reads
+        for (int kb = 0; kb < C::NKB; ++kb) s[kb] = mfma32(kf[kb][kk], qf[kk], s[kb]);
+      __builtin_amdgcn_sched_group_barrier(0x100, C::NKK, 1);  // block 0 reads
 #pragma unroll
-    for (int i = 0; i < C::NKK * (C::NKB - 1); ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);     // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);     // next block's read
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, C::NKK, 1);  // last block's MFMAs
-    if (key0 + C::KC > N) {  // the tail chunk: keys at or past N get -inf
-      // register r of block kb holds key key0 + kb*32 + 8*(r/4) + 4g + r%4
-      const int lim = N - key0 - 4 * g;
-#pragma unroll
-      for (int kb = 0; kb < C::NKB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (kb * 32 + 8 * (r >> 2) + (r & 3) >= lim) s[kb][r] = -INFINITY;
-    }
-    if (partial) {  // token-exact: keys outside the query's runs get -inf
-      const unsigned ok = lane_key_bits<C::NKB>(bctx, qi, qa, key0, g);
-      if (__ballot(ok != ~0u)) {  // some key of the wave's block is masked
+      for (int i = 0; i < C::NKK * (C::NKB - 1); ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);     // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);     // next block's read
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, C::NKK, 1);  // last block's MFMAs
+      if (key0 + C::KC > N) {  // the tail chunk: keys at or past N get -inf
+        // register r of block kb holds key key0 + kb*32 + 8*(r/4) + 4g + r%4
+        const int lim = N - key0 - 4 * g;
 #pragma unroll
         for (int kb = 0; kb < C::NKB; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r)
-            if (!((ok >> (16 * kb + r)) & 1u)) s[kb][r] = -INFINITY;
+            if (kb * 32 + 8 * (r >> 2) + (r & 3) >= lim) s[kb][r] = -INFINITY;
       }
-    }
-    float mx = -INFINITY;
+      if (partial) {  // token-exact: keys outside the query's runs get -inf
+        const unsigned ok = lane_key_bits<C::NKB>(bctx, qi, qa, key0, g);
+        if (__ballot(ok != ~0u)) {  // some key of the wave's block is masked
 #pragma unroll
-    for (int kb = 0; kb < C::NKB; ++kb)
+          for (int kb = 0; kb < C::NKB; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    const float m_new = pair_max(mx) * scale_log2;
-    if (__ballot(m_new > m_run + kSlack)) {
-      const bool mv = m_new > m_run + kSlack;
-      const float alpha = mv ? fast_exp2(m_run - m_new) : 1.f;
-      m_run = mv ? m_new : m_run;
-      l_run *= alpha;
-#pragma unroll
-      for (int db = 0; db < C::NDB; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-    }
-
-    bf16x8 pf[C::NKB][2];
-    float psum[4] = {0.f, 0.f, 0.f, 0.f};  // four partial sums: short add chains
-#pragma unroll
-    for (int kb = 0; kb < C::NKB; ++kb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = fast_exp2(fmaf(s[kb][r], scale_log2, -m_run));
-        psum[r & 3] += p;
-        pf[kb][r >> 3][r & 7] = bf16(p);
-      }
-    }
-    l_run += (psum[0] + psum[1]) + (psum[2] + psum[3]);
-
-    // O^T += V^T P^T
-#pragma unroll
-    for (int kb = 0; kb < C::NKB; ++kb) {
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-#pragma unroll
-        for (int db = 0; db < C::NDB; ++db) {
-          const int col = db * 32 + 16 * (G & 1) + 4 * (j & 3);
-          const int n0 = kb * 32 + ks * 16 + 4 * (G >> 1) + (j >> 2);
-          const bf16x4 lo = ld_tr(Vs + swz<D>(n0, col >> 3) + (col & 7));
-          const bf16x4 hi = ld_tr(Vs + swz<D>(n0 + 8, col >> 3) + (col & 7));
-          oacc[db] = mfma32(cat(lo, hi), pf[kb][ks], oacc[db]);
+            for (int r = 0; r < 16; ++r)
+              if (!((ok >> (16 * kb + r)) & 1u)) s[kb][r] = -INFINITY;
         }
       }
-    }
-    // transposing reads run four ahead of the products that consume them
-    constexpr int NPV = C::NDB * C::NKB * 2;
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 2);
+      float mx = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < NPV - 2; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 2);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 2, 2);
+      for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+      const float m_new = pair_max(mx) * scale_log2;
+      if (__ballot(m_new > m_run + kSlack)) {
+        const bool mv = m_new > m_run + kSlack;
+        const float alpha = mv ? fast_exp2(m_run - m_new) : 1.f;
+        m_run = mv ? m_new : m_run;
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+      }
+
+      bf16x8 pf[C::NKB][2];
+      float psum[4] = {0.f, 0.f, 0.f, 0.f};  // four partial sums: short add chains
+#pragma unroll
+      for (int kb = 0; kb < C::NKB; ++kb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p = fast_exp2(fmaf(s[kb][r], scale_log2, -m_run));
+          psum[r & 3] += p;
+          pf[kb][r >> 3][r & 7] = bf16(p);
+        }
+      }
+      l_run += (psum[0] + psum[1]) + (psum[2] + psum[3]);
+
+      // O^T += V^T P^T
+#pragma unroll
+      for (int kb = 0; kb < C::NKB; ++kb) {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+          for (int db = 0; db < C::NDB; ++db) {
+            const int col = db * 32 + 16 * (G & 1) + 4 * (j & 3);
+            const int n0 = kb * 32 + ks * 16 + 4 * (G >> 1) + (j >> 2);
+            const bf16x4 lo = ld_tr(Vs + swz<D>(n0, col >> 3) + (col & 7));
+            const bf16x4 hi = ld_tr(Vs + swz<D>(n0 + 8, col >> 3) + (col & 7));
+            oacc[db] = mfma32(cat(lo, hi), pf[kb][ks], oacc[db]);
+          }
+        }
+      }
+      // transposing reads run four ahead of the products that consume them
+      constexpr int NPV = C::NDB * C::NKB * 2;
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 2);
+#pragma unroll
+      for (int i = 0; i < NPV - 2; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 2);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 2);
+    }  // member
 
     wait_vmem();      // this wave's copies of chunk c + 1 have landed
     __syncthreads();  // ... everyone's, and chunk c is no longer read
@@ -277,19 +304,24 @@ __global__ __launch_bounds__(T / 32 * 64, 2) void radial_fwd_kernel(
   }
 }
 
-template <int D, int T, bool EXACT>
+template <int D, int T, bool EXACT, bool PAIR>
 hipError_t launch_fwd_t(const FwdArgs &a, hipStream_t stream) {
-  const int64_t works = (int64_t)a.BH * a.nb;
-  hipLaunchKernelGGL((radial_fwd_kernel<D, T, EXACT>), dim3((unsigned)works),
-                     dim3(FwdCfg<D, T>::NT), 0, stream, (const bf16 *)a.q, (const bf16 *)a.k,
-                     (const bf16 *)a.v, (bf16 *)a.o, a.lse, a.row_ptr, a.col_idx, a.N, a.nb,
-                     (int32_t)works, a.scale * kLog2e, a.mask);
+  const int64_t works = (int64_t)a.BH * (PAIR ? (a.nb + 1) / 2 : a.nb);
+  hipLaunchKernelGGL((radial_fwd_kernel<D, T, EXACT, PAIR>), dim3((unsigned)works),
+                     dim3(FwdCfg<D, T, PAIR>::NT), 0, stream, (const bf16 *)a.q,
+                     (const bf16 *)a.k, (const bf16 *)a.v, (bf16 *)a.o, a.lse, a.row_ptr,
+                     a.col_idx, a.pair_ptr, a.pair_idx, a.N, a.nb, (int32_t)works,
+                     a.scale * kLog2e, a.mask);
   return hipGetLastError();
 }
 
 template <int D, int T>
 hipError_t launch_fwd_t(const FwdArgs &a, hipStream_t stream) {
-  return a.mask.exact ? launch_fwd_t<D, T, true>(a, stream) : launch_fwd_t<D, T, false>(a, stream);
+  if (RADIAL_FWD_PAIR && a.pair_ptr)
+    return a.mask.exact ? launch_fwd_t<D, T, true, true>(a, stream)
+                        : launch_fwd_t<D, T, false, true>(a, stream);
+  return a.mask.exact ? launch_fwd_t<D, T, true, false>(a, stream)
+                      : launch_fwd_t<D, T, false, false>(a, stream);
 }
 
 hipError_t launch_fwd(const FwdArgs &a, hipStream_t stream) {

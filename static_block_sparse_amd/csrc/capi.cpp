@@ -42,7 +42,7 @@ void free_device(radial_layout *L) {
   }
   L->d_base = nullptr;
   L->d_row_ptr = L->d_col_idx = L->d_col_ptr = L->d_row_idx = L->d_col_order = nullptr;
-  L->d_band_rtab = nullptr;
+  L->d_band_rtab = L->d_pair_ptr = L->d_pair_idx = nullptr;
   L->device = -1;
 }
 
@@ -186,7 +186,8 @@ int radial_layout_upload(radial_layout *L) {
   if (L->d_base) free_device(L);
   if (forced_alloc_failure()) return fail(RADIAL_E_NOMEM, "allocation failure (forced by test hook)");
   const size_t nb1 = (size_t)L->nb + 1, nz = (size_t)L->nnz_tiles, nb = (size_t)L->nb;
-  const size_t words = 2 * nb1 + 2 * nz + nb + L->band_rtab.size();
+  const size_t words =
+      2 * nb1 + 2 * nz + nb + L->band_rtab.size() + L->pair_ptr.size() + L->pair_idx.size();
   void *p = nullptr;
   if (hipMalloc(&p, words * sizeof(int32_t)) != hipSuccess || !p) {
     (void)hipGetLastError();
@@ -216,7 +217,9 @@ int radial_layout_upload(radial_layout *L) {
                {&L->col_ptr, &L->d_col_ptr},
                {row_src, &L->d_row_idx},
                {&L->col_order, &L->d_col_order},
-               {&L->band_rtab, &L->d_band_rtab}};
+               {&L->band_rtab, &L->d_band_rtab},
+               {&L->pair_ptr, &L->d_pair_ptr},
+               {&L->pair_idx, &L->d_pair_idx}};
   for (auto &pt : parts) {
     const size_t cnt = pt.src->size();
     if (cnt && hipMemcpy(b + off, pt.src->data(), cnt * sizeof(int32_t),
@@ -280,6 +283,8 @@ int radial_attn_fwd(const radial_layout *L, int32_t B, int32_t H, int64_t N, int
   a.lse = lse;
   a.row_ptr = L->d_row_ptr;
   a.col_idx = L->d_col_idx;
+  a.pair_ptr = L->d_pair_ptr;
+  a.pair_idx = L->d_pair_idx;
   a.BH = B * H;
   a.N = static_cast<int32_t>(N);
   a.D = D;

@@ -6,6 +6,13 @@
 
 namespace radial {
 
+// Fields of an entry of the forward pass's pair lists (per pair of query
+// tiles 2p, 2p + 1, the sorted union of their key tiles): the key tile, a
+// membership bit per row (A = 2p, B = 2p + 1) and a partial-tile bit per row.
+constexpr int32_t kPairTile = (1 << 27) - 1;
+constexpr int32_t kPairInA = 1 << 27, kPairInB = 1 << 28;
+constexpr int32_t kPairPartA = 1 << 29, kPairPartB = 1 << 30;
+
 // What the kernels need of the mask to apply it token by token inside the
 // tiles a token-exact layout marks partial (bit 31 of the tile indices).
 struct MaskGeom {
@@ -31,6 +38,8 @@ struct FwdArgs {
   void *o;
   float *lse;
   const int32_t *row_ptr, *col_idx;  // device CSR of the layout
+  // per pair of query tiles: the union of their key tiles (see layout.h)
+  const int32_t *pair_ptr, *pair_idx;
   int32_t BH, N, D, T, nb;
   float scale;
   MaskGeom mask;

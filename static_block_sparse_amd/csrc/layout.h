@@ -28,12 +28,17 @@ struct radial_layout {
   std::vector<int32_t> row_ptr, col_idx;  // CSR: key tiles per query tile
   std::vector<int32_t> col_ptr, row_idx;  // CSC: query tiles per key tile
   std::vector<int32_t> col_order;         // key tiles, longest column first
+  // forward pass, per pair of query tiles (2p, 2p + 1): the sorted union of
+  // their key tiles; entry = key tile | kPairInA | kPairInB (member of row
+  // 2p / 2p + 1) | kPairPartA | kPairPartB (partial in that row).  Built when
+  // the tile index fits below 2^27 (every supported tile size).
+  std::vector<int32_t> pair_ptr, pair_idx;
   // full[t] = 1 when every valid token pair of CSR tile t is allowed (no
   // masking needed under token-exact semantics), else 0; full_csc in CSC order
   std::vector<uint8_t> full, full_csc;
 
   // device copy (one allocation): row_ptr | col_idx | col_ptr | row_idx |
-  // col_order | band_rtab
+  // col_order | band_rtab | pair_ptr | pair_idx
   int device = -1;
   void *d_base = nullptr;
   const int32_t *d_row_ptr = nullptr;
@@ -42,6 +47,8 @@ struct radial_layout {
   const int32_t *d_row_idx = nullptr;
   const int32_t *d_col_order = nullptr;
   const int32_t *d_band_rtab = nullptr;
+  const int32_t *d_pair_ptr = nullptr;
+  const int32_t *d_pair_idx = nullptr;
 };
 
 namespace radial {

@@ -39,11 +39,13 @@
 // key frame, the keys every query of the tile may attend, and a kept tile
 // whose keys lie inside that set in each of its frames is full.
 #include <algorithm>
+#include <climits>
 #include <cstdint>
 #include <string>
 #include <utility>
 #include <vector>
 
+#include "kernels.h"
 #include "layout.h"
 #include "radial.h"
 
@@ -236,6 +238,36 @@ std::string build_layout(int64_t frames, int64_t s, int32_t T, uint32_t flags,
         }
         L.full[t] = full ? 1 : 0;
       }
+    }
+  }
+
+  // forward pairs: the union of the key tiles of query tiles 2p and 2p + 1
+  L.pair_ptr.clear();
+  L.pair_idx.clear();
+  if (nb <= kPairTile) {
+    const int64_t np = (nb + 1) / 2;
+    L.pair_ptr.assign(np + 1, 0);
+    L.pair_idx.reserve(L.nnz_tiles);
+    for (int64_t pr = 0; pr < np; ++pr) {
+      const int64_t ua = 2 * pr, ub = 2 * pr + 1;
+      int32_t i = L.row_ptr[ua], ie = L.row_ptr[ua + 1];
+      int32_t j = ub < nb ? L.row_ptr[ub] : 0, je = ub < nb ? L.row_ptr[ub + 1] : 0;
+      while (i < ie || j < je) {
+        const int32_t a = i < ie ? L.col_idx[i] : INT32_MAX;
+        const int32_t b = j < je ? L.col_idx[j] : INT32_MAX;
+        const int32_t v = a < b ? a : b;
+        int32_t e = v;
+        if (a == v) {
+          e |= kPairInA | (L.full[i] ? 0 : kPairPartA);
+          ++i;
+        }
+        if (b == v) {
+          e |= kPairInB | (L.full[j] ? 0 : kPairPartB);
+          ++j;
+        }
+        L.pair_idx.push_back(e);
+      }
+      L.pair_ptr[pr + 1] = static_cast<int32_t>(L.pair_idx.size());
     }
   }
 
