@@ -24,6 +24,9 @@
 #include "device_common.h"
 #include "kernels.h"
 
+#ifndef RADIAL_DQ_PAIR
+#define RADIAL_DQ_PAIR 1  // dQ over pairs of query tiles sharing K/V chunks
+#endif
 #ifndef RADIAL_BWD_XCD_BLOCK
 #define RADIAL_BWD_XCD_BLOCK 16  // tiles per XCD block (see xcd_remap)
 #endif
@@ -459,9 +462,10 @@ __global__ __launch_bounds__(T / 32 * 64, 1) void radial_bwd_dkdv_kernel(
 //    buffered: S^T = K Q^T and dP^T = V dO^T read K and V row-major, and
 //    dQ^T += K^T dS^T reads K^T with transposing loads.
 // ---------------------------------------------------------------------------
-template <int D, int T>
+template <int D, int T, bool PAIR>
 struct DqCfg {
-  static constexpr int NW = T / 32;
+  static constexpr int NWR = T / 32;                // waves per query tile
+  static constexpr int NW = NWR * (PAIR ? 2 : 1);   // waves per workgroup
   static constexpr int NT = NW * 64;
   static constexpr int KC = 64;
   static constexpr int CPT = T / KC;
@@ -472,28 +476,36 @@ struct DqCfg {
   using Copier = TileCopier<D, KC, NW>;
 };
 
-template <int D, int T, bool EXACT>
-__global__ __launch_bounds__(T / 32 * 64, 2) void radial_bwd_dq_kernel(
+template <int D, int T, bool EXACT, bool PAIR>
+__global__ __launch_bounds__(T / 32 * 64 * (PAIR ? 2 : 1),
+                             PAIR ? 256 / (T / 32 * 64) : 2) void radial_bwd_dq_kernel(
     const bf16 *__restrict__ Q, const bf16 *__restrict__ K, const bf16 *__restrict__ V,
     const bf16 *__restrict__ dO, const float *__restrict__ NLse2,
     const float *__restrict__ NDelta, bf16 *__restrict__ dQ,
-    const int32_t *__restrict__ row_ptr, const int32_t *__restrict__ col_idx, int32_t N,
+    const int32_t *__restrict__ row_ptr, const int32_t *__restrict__ col_idx,
+    const int32_t *__restrict__ pair_ptr, const int32_t *__restrict__ pair_idx, int32_t N,
     int32_t nb, int32_t n_work, float scale_log2, float scale, MaskGeom mg) {
-  using C = DqCfg<D, T>;
+  using C = DqCfg<D, T, PAIR>;
   __shared__ __attribute__((aligned(1024))) bf16 lds[4 * C::CHUNK];  // K0 V0 K1 V1
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c32 = lane & 31, g = lane >> 5;
+  // work item: one query tile, or with PAIR the query tiles 2p (waves
+  // [0, NWR)) and 2p + 1 over the union of their key tiles, so every staged
+  // K/V chunk serves twice the queries (as in the forward pass)
+  const int nwork_head = PAIR ? (nb + 1) / 2 : nb;
   const int work = xcd_remap(blockIdx.x, n_work, RADIAL_BWD_XCD_BLOCK);
-  const int bh = work / nb;
-  const int u = work - bh * nb;
+  const int bh = work / nwork_head;
+  const int wi = work - bh * nwork_head;
+  const int sub = PAIR ? wave / C::NWR : 0;
+  const int u = PAIR ? 2 * wi + sub : wi;
   const int64_t base = (int64_t)bh * N * D;
   const bf16 *Kb = K + base;
   const bf16 *Vb = V + base;
 
-  const int qrow = u * T + wave * 32 + c32;
-  const bool q_ok = qrow < N;
+  const int qrow = u * T + (wave % C::NWR) * 32 + c32;
+  const bool q_ok = u < nb && qrow < N;
   bf16x8 qf[C::NKK], dof[C::NKK];
 #pragma unroll
   for (int kk = 0; kk < C::NKK; ++kk) {
@@ -508,15 +520,16 @@ __global__ __launch_bounds__(T / 32 * 64, 2) void radial_bwd_dq_kernel(
 #pragma unroll
   for (int db = 0; db < C::NDB; ++db) adq[db] = zero16();
 
-  const int t_begin = row_ptr[u], t_end = row_ptr[u + 1];
+  // chunk list over the CSR row or the pair list (entries as in the forward)
+  const int32_t *lptr = PAIR ? pair_ptr : row_ptr;
+  const int32_t *lidx = PAIR ? pair_idx : col_idx;
+  constexpr int32_t TMASK = PAIR ? kPairTile : 0x7fffffff;
+  const int t_begin = lptr[wi], t_end = lptr[wi + 1];
   int nch = (t_end - t_begin) * C::CPT;
-  if (t_end > t_begin && (col_idx[t_end - 1] & 0x7fffffff) == nb - 1)
+  if (t_end > t_begin && (lidx[t_end - 1] & TMASK) == nb - 1)
     nch -= C::CPT - (N - (nb - 1) * T + C::KC - 1) / C::KC;
-  // first key of chunk c, with bit 31 set when its tile is marked partial
-  auto key_of = [&](int c) {
-    const int raw = col_idx[t_begin + c / C::CPT];
-    return ((raw & 0x7fffffff) * T + (c % C::CPT) * C::KC) | (raw & int(0x80000000));
-  };
+  auto chunk_raw = [&](int c) { return lidx[t_begin + c / C::CPT]; };
+  auto key_of = [&](int raw, int c) { return (raw & TMASK) * T + (c % C::CPT) * C::KC; };
   // this lane's query as (frame, position), for the token predicate
   const int qi = qrow / mg.s, qa = qrow - (qrow / mg.s) * mg.s;
   // token-exact: the mask's per-band table, read by the predicate from LDS
@@ -532,9 +545,9 @@ __global__ __launch_bounds__(T / 32 * 64, 2) void radial_bwd_dq_kernel(
     cp.copy(kd + C::CHUNK, Vb + (int64_t)k0 * D, N - k0, wave);
   };
 
-  int key_n = nch > 0 ? key_of(0) : 0;   // first keys of chunks c and c + 1
-  int key_nn = nch > 1 ? key_of(1) : 0;
-  if (nch > 0) issue(0, key_n & 0x7fffffff);
+  int raw_n = nch > 0 ? chunk_raw(0) : 0;   // list entries of chunks c and c + 1
+  int raw_nn = nch > 1 ? chunk_raw(1) : 0;
+  if (nch > 0) issue(0, key_of(raw_n, 0));
   wait_vmem();  // Q, dO fragments, LSE, Delta and the first chunk
   if constexpr (EXACT) {
     if (threadIdx.x < 64) lds_rtab[threadIdx.x] = rtab_v;
@@ -543,60 +556,64 @@ __global__ __launch_bounds__(T / 32 * 64, 2) void radial_bwd_dq_kernel(
   const BandCtx bctx = make_band_ctx(mg, lds_rtab);
 
   for (int c = 0; c < nch; ++c) {
-    const int key0 = key_n & 0x7fffffff;
-    const bool partial = EXACT && key_n < 0;
-    if (c + 1 < nch) issue(c + 1, key_nn & 0x7fffffff);  // lands during this chunk
-    const int key_3 = c + 2 < nch ? key_of(c + 2) : 0;
-    // token-exact: this lane's allowed keys of the chunk
-    const unsigned ok =
-        partial ? lane_key_bits<C::NKB>(bctx, qi, qa, key0, g) : ~0u;
-    const bool masked = partial && __ballot(ok != ~0u);  // some key of the block is masked
+    const int key0 = key_of(raw_n, c);
+    // this wave's tile takes part in the chunk (always without PAIR)
+    const bool member = PAIR ? ((raw_n >> (27 + sub)) & 1) != 0 : true;
+    const bool partial = EXACT && (PAIR ? ((raw_n >> (29 + sub)) & 1) != 0 : raw_n < 0);
+    if (c + 1 < nch) issue(c + 1, key_of(raw_nn, c + 1));  // lands during this chunk
+    const int raw_3 = c + 2 < nch ? chunk_raw(c + 2) : 0;
     const bf16 *Ks = lds + (c & 1) * 2 * C::CHUNK;
     const bf16 *Vs = Ks + C::CHUNK;
 
+    if (member) {
+      // token-exact: this lane's allowed keys of the chunk
+      const unsigned ok =
+          partial ? lane_key_bits<C::NKB>(bctx, qi, qa, key0, g) : ~0u;
+      const bool masked = partial && __ballot(ok != ~0u);  // some key of the block is masked
+
 #pragma unroll
-    for (int kb = 0; kb < C::NKB; ++kb) {
-      bf16x8 ka[C::NKK], va[C::NKK];
+      for (int kb = 0; kb < C::NKB; ++kb) {
+        bf16x8 ka[C::NKK], va[C::NKK];
 #pragma unroll
-      for (int kk = 0; kk < C::NKK; ++kk) {
-        ka[kk] = ld8(Ks + swz<D>(kb * 32 + c32, 2 * kk + g));
-        va[kk] = ld8(Vs + swz<D>(kb * 32 + c32, 2 * kk + g));
+        for (int kk = 0; kk < C::NKK; ++kk) {
+          ka[kk] = ld8(Ks + swz<D>(kb * 32 + c32, 2 * kk + g));
+          va[kk] = ld8(Vs + swz<D>(kb * 32 + c32, 2 * kk + g));
+        }
+        // dP starts from -Delta, so the products give dP - Delta directly
+        f32x16 s = zero16(), dp;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dp[r] = ndl;
+#pragma unroll
+        for (int kk = 0; kk < C::NKK; ++kk) {
+          s = mfma32(ka[kk], qf[kk], s);
+          dp = mfma32(va[kk], dof[kk], dp);
+        }
+        // register r holds key kb*32 + 8*(r/4) + 4g + r%4 of the chunk
+        if (masked) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (!((ok >> (16 * kb + r)) & 1u)) s[r] = -INFINITY;
+        }
+        bf16x8 dsb[2];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p = fast_exp2(fmaf(s[r], scale_log2, nl2));
+          dsb[r >> 3][r & 7] = bf16(p * dp[r]);
+        }
+        // consecutive products share their dS operand (less switching)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+          for (int db = 0; db < C::NDB; ++db)
+            adq[db] = mfma32(ld_trA<D>(Ks, db, kb, ks, lane), dsb[ks], adq[db]);
       }
-      // dP starts from -Delta, so the products give dP - Delta directly
-      f32x16 s = zero16(), dp;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) dp[r] = ndl;
-#pragma unroll
-      for (int kk = 0; kk < C::NKK; ++kk) {
-        s = mfma32(ka[kk], qf[kk], s);
-        dp = mfma32(va[kk], dof[kk], dp);
-      }
-      // register r holds key kb*32 + 8*(r/4) + 4g + r%4 of the chunk
-      if (masked) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (!((ok >> (16 * kb + r)) & 1u)) s[r] = -INFINITY;
-      }
-      bf16x8 dsb[2];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = fast_exp2(fmaf(s[r], scale_log2, nl2));
-        dsb[r >> 3][r & 7] = bf16(p * dp[r]);
-      }
-      // consecutive products share their dS operand (less switching)
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int db = 0; db < C::NDB; ++db)
-          adq[db] = mfma32(ld_trA<D>(Ks, db, kb, ks, lane), dsb[ks], adq[db]);
-    }
+    }  // member
 
     wait_vmem();      // chunk c + 1 has landed here ...
     __syncthreads();  // ... and everywhere; chunk c is no longer read
-    key_n = key_nn;
-    key_nn = key_3;
+    raw_n = raw_nn;
+    raw_nn = raw_3;
   }
-  (void)key_n;
 
   if (q_ok) {
     bf16 *row = dQ + base + (int64_t)qrow * D;
@@ -613,7 +630,7 @@ __global__ __launch_bounds__(T / 32 * 64, 2) void radial_bwd_dq_kernel(
   }
 }
 
-template <int D, int T, bool EXACT>
+template <int D, int T, bool EXACT, bool PAIR>
 hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t stream) {
   const int64_t rows = (int64_t)a.BH * a.N;
   constexpr int RPB = 256 / (D / 8);
@@ -631,16 +648,22 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t stream) {
                      sl2, a.scale, a.mask);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((radial_bwd_dq_kernel<D, T, EXACT>), dim3((unsigned)works),
-                     dim3(DqCfg<D, T>::NT), 0, stream, (const bf16 *)a.q, (const bf16 *)a.k,
-                     (const bf16 *)a.v, (const bf16 *)a.dout, a.nlse2, a.ndelta, (bf16 *)a.dq,
-                     a.row_ptr, a.col_idx, a.N, a.nb, (int32_t)works, sl2, a.scale, a.mask);
+  const int64_t dq_works = (int64_t)a.BH * (PAIR ? (a.nb + 1) / 2 : a.nb);
+  hipLaunchKernelGGL((radial_bwd_dq_kernel<D, T, EXACT, PAIR>), dim3((unsigned)dq_works),
+                     dim3(DqCfg<D, T, PAIR>::NT), 0, stream, (const bf16 *)a.q,
+                     (const bf16 *)a.k, (const bf16 *)a.v, (const bf16 *)a.dout, a.nlse2,
+                     a.ndelta, (bf16 *)a.dq, a.row_ptr, a.col_idx, a.pair_ptr, a.pair_idx, a.N,
+                     a.nb, (int32_t)dq_works, sl2, a.scale, a.mask);
   return hipGetLastError();
 }
 
 template <int D, int T>
 hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t stream) {
-  return a.mask.exact ? launch_bwd_t<D, T, true>(a, stream) : launch_bwd_t<D, T, false>(a, stream);
+  if (RADIAL_DQ_PAIR && a.pair_ptr)
+    return a.mask.exact ? launch_bwd_t<D, T, true, true>(a, stream)
+                        : launch_bwd_t<D, T, false, true>(a, stream);
+  return a.mask.exact ? launch_bwd_t<D, T, true, false>(a, stream)
+                      : launch_bwd_t<D, T, false, false>(a, stream);
 }
 
 hipError_t launch_bwd(const BwdArgs &a, hipStream_t stream) {

@@ -343,6 +343,8 @@ int radial_attn_bwd(const radial_layout *L, int32_t B, int32_t H, int64_t N, int
   a.nlse2 = reinterpret_cast<float *>(static_cast<char *>(workspace) + need / 2);
   a.row_ptr = L->d_row_ptr;
   a.col_idx = L->d_col_idx;
+  a.pair_ptr = L->d_pair_ptr;
+  a.pair_idx = L->d_pair_idx;
   a.col_ptr = L->d_col_ptr;
   a.row_idx = L->d_row_idx;
   a.col_order = L->d_col_order;

@@ -52,6 +52,7 @@ struct BwdArgs {
   float *ndelta;                     // workspace: -rowsum(dO * O), fp32 [BH, N]
   float *nlse2;                      // workspace: -LSE * log2(e), fp32 [BH, N]
   const int32_t *row_ptr, *col_idx;  // CSR (dQ pass)
+  const int32_t *pair_ptr, *pair_idx;  // pair lists (dQ pass, see above)
   const int32_t *col_ptr, *row_idx;  // CSC (dK/dV pass)
   const int32_t *col_order;          // key tiles, longest column first
   int32_t BH, N, D, T, nb;

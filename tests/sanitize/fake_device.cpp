@@ -58,6 +58,35 @@ void check_mask(const radial::MaskGeom &m) {
   check(m.s_shift >= 31 && m.s_shift <= 62, "division shift");
 }
 
+// pair lists: for query tiles 2p and 2p + 1, the sorted union of their CSR
+// rows, each entry marked with its membership bits
+void check_pairs(const int32_t *row_ptr, const int32_t *col_idx, const int32_t *pair_ptr,
+                 const int32_t *pair_idx, int32_t nb) {
+  check(pair_ptr != nullptr && pair_idx != nullptr, "pair lists uploaded");
+  if (!pair_ptr || !pair_idx) return;
+  const int32_t np = (nb + 1) / 2;
+  check(pair_ptr[0] == 0, "pair lists start");
+  for (int32_t p = 0; p < np; ++p) {
+    int32_t i = row_ptr[2 * p], ie = row_ptr[2 * p + 1];
+    int32_t j = 2 * p + 1 < nb ? row_ptr[2 * p + 1] : 0;
+    int32_t je = 2 * p + 1 < nb ? row_ptr[2 * p + 2] : 0;
+    int32_t prev = -1;
+    for (int32_t t = pair_ptr[p]; t < pair_ptr[p + 1]; ++t) {
+      const int32_t e = pair_idx[t], v = e & radial::kPairTile;
+      check(v > prev && v < nb, "pair list sorted, in range");
+      prev = v;
+      const bool in_a = i < ie && (col_idx[i] & 0x7fffffff) == v;
+      const bool in_b = j < je && (col_idx[j] & 0x7fffffff) == v;
+      check(in_a || in_b, "pair entry comes from a row");
+      check(((e & radial::kPairInA) != 0) == in_a && ((e & radial::kPairInB) != 0) == in_b,
+            "membership bits");
+      if (in_a) ++i;
+      if (in_b) ++j;
+    }
+    check(i == ie && j == je, "pair list covers both rows");
+  }
+}
+
 }  // namespace
 
 extern "C" int fake_device_failures() { return g_fail; }
@@ -96,31 +125,7 @@ hipError_t launch_fwd(const FwdArgs &a, hipStream_t) {
   write_range(a.o, x);
   write_range(a.lse, r);
   check_lists(a.row_ptr, a.col_idx, a.nb, "forward CSR");
-  // pair lists: for query tiles 2p and 2p + 1, the sorted union of their
-  // CSR rows, each entry marked with its membership and partial bits
-  check(a.pair_ptr != nullptr && a.pair_idx != nullptr, "pair lists uploaded");
-  if (a.pair_ptr && a.pair_idx) {
-    const int32_t np = (a.nb + 1) / 2;
-    check(a.pair_ptr[0] == 0, "pair lists start");
-    for (int32_t p = 0; p < np; ++p) {
-      int32_t i = a.row_ptr[2 * p], ie = a.row_ptr[2 * p + 1];
-      int32_t j = 2 * p + 1 < a.nb ? a.row_ptr[2 * p + 1] : 0;
-      int32_t je = 2 * p + 1 < a.nb ? a.row_ptr[2 * p + 2] : 0;
-      int32_t t = a.pair_ptr[p], prev = -1;
-      for (; t < a.pair_ptr[p + 1]; ++t) {
-        const int32_t e = a.pair_idx[t], v = e & kPairTile;
-        check(v > prev && v < a.nb, "pair list sorted, in range");
-        prev = v;
-        const bool in_a = i < ie && (a.col_idx[i] & 0x7fffffff) == v;
-        const bool in_b = j < je && (a.col_idx[j] & 0x7fffffff) == v;
-        check(in_a || in_b, "pair entry comes from a row");
-        check(((e & kPairInA) != 0) == in_a && ((e & kPairInB) != 0) == in_b, "membership bits");
-        if (in_a) ++i;
-        if (in_b) ++j;
-      }
-      check(i == ie && j == je, "pair list covers both rows");
-    }
-  }
+  check_pairs(a.row_ptr, a.col_idx, a.pair_ptr, a.pair_idx, a.nb);
   check_mask(a.mask);
   return hipSuccess;
 }
@@ -136,6 +141,7 @@ hipError_t launch_bwd(const BwdArgs &a, hipStream_t) {
   check(a.nlse2 >= a.ndelta + size_t(a.BH) * a.N, "workspace arrays overlap");
   check_lists(a.row_ptr, a.col_idx, a.nb, "backward CSR");
   check_lists(a.col_ptr, a.row_idx, a.nb, "backward CSC");
+  check_pairs(a.row_ptr, a.col_idx, a.pair_ptr, a.pair_idx, a.nb);
   // col_order: a permutation of the key tiles
   unsigned char *seen = static_cast<unsigned char *>(std::calloc(a.nb, 1));
   for (int32_t i = 0; i < a.nb; ++i) {
