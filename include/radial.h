@@ -202,8 +202,8 @@ void radial_layout_destroy(radial_layout *L);
  *   o       : bf16 [B, H, N, D] output (rounded to nearest even).
  *   lse     : fp32 [B, H, N] output, natural-log log-sum-exp of the scaled,
  *             masked logits of each query row (used by the backward pass).
- * N must equal the layout's n; (D, block_size) must be (64, 64) or
- * (128, 128); B, H >= 1; scale finite and > 0 (usually 1/sqrt(D)).
+ * N must equal the layout's n; (D, block_size) must be (64, 64),
+ * (64, 128) or (128, 128); B, H >= 1; scale finite and > 0 (usually 1/sqrt(D)).
  * Products run on bf16 MFMA with fp32 accumulation and an fp32 online
  * softmax; the probabilities are rounded to bf16 before the P V product.
  */

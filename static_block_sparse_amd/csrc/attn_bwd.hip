@@ -668,6 +668,7 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t stream) {
 
 hipError_t launch_bwd(const BwdArgs &a, hipStream_t stream) {
   if (a.D == 64 && a.T == 64) return launch_bwd_t<64, 64>(a, stream);
+  if (a.D == 64 && a.T == 128) return launch_bwd_t<64, 128>(a, stream);
   if (a.D == 128 && a.T == 128) return launch_bwd_t<128, 128>(a, stream);
   return hipErrorInvalidValue;
 }

@@ -326,6 +326,7 @@ hipError_t launch_fwd_t(const FwdArgs &a, hipStream_t stream) {
 
 hipError_t launch_fwd(const FwdArgs &a, hipStream_t stream) {
   if (a.D == 64 && a.T == 64) return launch_fwd_t<64, 64>(a, stream);
+  if (a.D == 64 && a.T == 128) return launch_fwd_t<64, 128>(a, stream);
   if (a.D == 128 && a.T == 128) return launch_fwd_t<128, 128>(a, stream);
   return hipErrorInvalidValue;
 }

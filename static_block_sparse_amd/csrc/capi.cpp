@@ -54,10 +54,11 @@ int check_common(const radial_layout *L, int32_t B, int32_t H, int64_t N, int32_
   if (N != L->n)
     return fail(RADIAL_E_SHAPE, "N = " + std::to_string(N) + " but the layout has n = " +
                                     std::to_string(L->n) + " (frames * tokens_per_frame)");
-  if (!((D == 64 && L->block == 64) || (D == 128 && L->block == 128)))
+  if (!((D == 64 && L->block == 64) || (D == 64 && L->block == 128) ||
+        (D == 128 && L->block == 128)))
     return fail(RADIAL_E_UNSUPPORTED, "(D, block_size) = (" + std::to_string(D) + ", " +
                                           std::to_string(L->block) +
-                                          ") not supported; use (64, 64) or (128, 128)");
+                                          ") not supported; use (64, 64), (64, 128) or (128, 128)");
   if (!std::isfinite(scale) || !(scale > 0.f))
     return fail(RADIAL_E_INVALID, "scale must be finite and > 0");
   if ((int64_t)B * H > (int64_t(1) << 31) / (L->nb > 0 ? L->nb : 1))

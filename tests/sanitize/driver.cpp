@@ -96,6 +96,18 @@ void exercise(const Shape &sh) {
     std::free(ws);
   }
   for (void *p : {q, k, v, o, dout, dq, dk, dv, static_cast<void *>(lse)}) std::free(p);
+  if (sh.T == 128) {  // head dim 64 on 128-wide tiles
+    const size_t x64 = size_t(B) * H * n * 64 * 2;
+    void *a = block(x64), *b = block(x64), *c = block(x64), *d = block(x64), *e = block(x64);
+    void *f = block(x64), *g2 = block(x64), *h = block(x64);
+    float *l64 = static_cast<float *>(block(r));
+    EXPECT(radial_attn_fwd(L, B, H, n, 64, sc, a, b, c, d, l64, nullptr) == RADIAL_OK);
+    const size_t ws_bytes = radial_attn_bwd_workspace_bytes(L, B, H, n, 64);
+    void *ws = block(ws_bytes);
+    EXPECT(radial_attn_bwd(L, B, H, n, 64, sc, a, b, c, d, l64, e, f, g2, h, ws, ws_bytes,
+                           nullptr) == RADIAL_OK);
+    for (void *p : {a, b, c, d, e, f, g2, h, ws, static_cast<void *>(l64)}) std::free(p);
+  }
   radial_layout_destroy(L);
 }
 

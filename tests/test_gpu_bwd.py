@@ -38,6 +38,8 @@ def _say(*a):
     (7, 100, 64, 64, 1, 2),      # ragged: last tile 60 rows
     (3, 40, 128, 128, 1, 1),     # one partial tile
     (66, 256, 128, 128, 1, 1),   # the training workload's frame count at s = 256
+    (5, 300, 128, 64, 1, 2),     # head dim 64 with 128-wide tiles
+    (9, 100, 128, 64, 2, 1),     # head dim 64 with 128-wide tiles, odd number of tiles
 ])
 def test_backward_small(f, s, T, D, B, H):
     N = f * s

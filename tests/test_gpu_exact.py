@@ -40,6 +40,7 @@ SHAPES = [
     (7, 100, 64, 64, 1, 2),      # ragged; 64-tiles span frames
     (3, 40, 128, 128, 1, 1),     # a single partial tile
     (40, 20, 64, 64, 1, 1),      # narrow bands: most kept tiles partial
+    (40, 20, 128, 64, 1, 1),     # head dim 64 with 128-wide tiles
     (300, 2, 64, 64, 1, 1),      # width below one: the sampled diagonal
     (33, 36, 128, 128, 1, 1),    # 3-4 frames per tile
 ]

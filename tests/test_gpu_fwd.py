@@ -62,6 +62,8 @@ def test_tiny_workload_all_heads():
     (7, 100, 64, 64, 1, 2),      # N = 700: last tile 60 rows; 64-tiles span frames
     (3, 40, 128, 128, 1, 1),     # a single, partial tile (N = 120 < T)
     (40, 20, 64, 64, 1, 1),      # many frames, narrow bands, rows of very different length
+    (5, 300, 128, 64, 1, 2),     # head dim 64 with 128-wide tiles; ragged last tile
+    (9, 100, 128, 64, 2, 1),     # head dim 64 with 128-wide tiles; odd number of tiles
     (300, 2, 64, 64, 1, 1),      # tiny frames: the width-below-one sampling fires
 ])
 def test_ragged_shapes(f, s, T, D, B, H):
@@ -126,8 +128,8 @@ def test_rejects_bad_inputs_on_gpu():
     q = torch.zeros((1, 1, 2048, 64), dtype=torch.bfloat16, device="cuda")
     with pytest.raises(sba.RadialError):
         sba.attn_fwd(q, q, q, sba.Layout(8, 255, 64))
-    with pytest.raises(sba.RadialError):
-        sba.attn_fwd(q, q, q, sba.Layout(8, 256, 128))
+    with pytest.raises(sba.RadialError):  # (D, block_size) = (64, 32): not supported
+        sba.attn_fwd(q, q, q, sba.Layout(8, 256, 32))
     # misaligned pointer: a view offset by one element
     raw = torch.zeros(2048 * 64 + 8, dtype=torch.bfloat16, device="cuda")
     lib = sba.lib()
