@@ -229,7 +229,7 @@ int radial_layout_upload(radial_layout *L) {
       (void)hipGetLastError();
       return fail(RADIAL_E_HIP, "hipMemcpy of the layout failed");
     }
-    *pt.dst = b + off;
+    *pt.dst = cnt ? b + off : nullptr;  // empty arrays (pair lists not built) stay null
     off += cnt;
   }
   L->d_base = p;
