@@ -249,14 +249,23 @@ __global__ __launch_bounds__(T / 32 * 64, 1) void radial_bwd_dkdv_kernel(
   // read in slot 1, or 0 without stage 3); a scheduling barrier after each slot
   // keeps that order.  With one wave per SIMD, LDS latency is hidden only by
   // this read-ahead and the vector work only by this interleaving.
-  auto step = [&](auto F1, auto F2, auto F3, int b1, int m1, int b2, int m2, int b3, int m3,
-                  Blk &sd_new, const Blk &sd_old, bf16x8 (&pd_new)[2][2],
-                  const bf16x8 (&pd_old)[2][2], unsigned okm) __attribute__((always_inline)) {
+  // The first RA operands of a step with stage 3 are carried in `pre`: the
+  // step before reads them in its last slots (flag FN, with the next step's
+  // stage-3 buffer b3n and half m3n), and the step takes them from there
+  // (flag FP), so no step starts by waiting for LDS.  Those operands belong
+  // to a chunk that landed at least one barrier earlier and whose buffer is
+  // refilled two barriers later.
+  constexpr int RA = 4;                                 // read-ahead (slots)
+  auto step = [&](auto F1, auto F2, auto F3, auto FP, auto FN, int b1, int m1, int b2, int m2,
+                  int b3, int m3, int b3n, int m3n, bf16x8 (&pre)[RA], Blk &sd_new,
+                  const Blk &sd_old, bf16x8 (&pd_new)[2][2], const bf16x8 (&pd_old)[2][2],
+                  unsigned okm) __attribute__((always_inline)) {
     constexpr bool s1 = decltype(F1)::value, s2 = decltype(F2)::value,
                    s3 = decltype(F3)::value;
+    constexpr bool from_pre = decltype(FP)::value, to_pre = decltype(FN)::value;
     constexpr int NM = 4 * C::NDB;                      // products per stage
     constexpr int N3 = s3 ? NM : 0, NSL = N3 + (s1 ? NM : 0);
-    constexpr int RA = 4;                               // read-ahead (slots)
+    static_assert(!from_pre || N3 >= RA, "carried operands are stage-3 operands");
     const bf16 *Qs3 = lds_q + b3 * C::CHUNK, *dOs3 = lds_do + b3 * C::CHUNK;
     const bf16 *Qs1 = lds_q + b1 * C::CHUNK, *dOs1 = lds_do + b1 * C::CHUNK;
     const float *rt2 = lds_r + b2 * 2 * C::MC + 32 * m2;           // -LSE log2(e), stage 2
@@ -274,6 +283,12 @@ __global__ __launch_bounds__(T / 32 * 64, 1) void radial_bwd_dkdv_kernel(
       }
       const int kk = (i - N3) / 2;
       return ld8((((i - N3) % 2) ? dOs1 : Qs1) + m1 * 32 * D + soff[kk]);
+    };
+    // stage-3 operand i < RA of the next step
+    auto frag_next = [&](int i) __attribute__((always_inline)) {
+      const int db = i % C::NDB, ks = i / (2 * C::NDB), w = (i / C::NDB) % 2;
+      const bf16 *t = (w ? lds_q : lds_do) + b3n * C::CHUNK + (m3n * 32 + ks * 16) * D;
+      return cat(ld_tr(t + toff[db][0]), ld_tr(t + toff[db][1]));
     };
     auto product = [&](int i, bf16x8 a) __attribute__((always_inline)) {
       if (i < N3) {
@@ -324,7 +339,7 @@ __global__ __launch_bounds__(T / 32 * 64, 1) void radial_bwd_dkdv_kernel(
     constexpr int SPAN = SEND > S0 ? SEND - S0 : 1;
     bf16x8 fr[NSL > 0 ? NSL : 1];
 #pragma unroll
-    for (int i = 0; i < RA && i < NSL; ++i) fr[i] = frag(i);
+    for (int i = 0; i < RA && i < NSL; ++i) fr[i] = from_pre ? pre[i] : frag(i);
 #pragma unroll
     for (int i = 0; i < NSL; ++i) {
       if constexpr (s2) {
@@ -337,7 +352,10 @@ __global__ __launch_bounds__(T / 32 * 64, 1) void radial_bwd_dkdv_kernel(
       if constexpr (s1) {
         if (i == (N3 > 0 ? 1 : 0)) nd_read();
       }
-      if (i + RA < NSL) fr[i + RA] = frag(i + RA);
+      if (i + RA < NSL)
+        fr[i + RA] = frag(i + RA);
+      else if constexpr (to_pre)
+        pre[i + RA - NSL] = frag_next(i + RA - NSL);
       product(i, fr[i]);
       if constexpr (s2) {
         // pairs [e0, e1) go with slot i
@@ -404,11 +422,13 @@ __global__ __launch_bounds__(T / 32 * 64, 1) void radial_bwd_dkdv_kernel(
     __syncthreads();
   };
 
+  bf16x8 pre[RA];  // first operands of the next step
   if (nch > 0) {
     // chunk iteration 0: steps 0 and 1
     if (nch > 2) issue(2, row_c);
-    step(YES, NO, NO, 0, 0, 0, 0, 0, 0, sdA, sdB, pdB, pdA, ~0u);
-    step(YES, YES, NO, 0, 1, 0, 0, 0, 0, sdB, sdA, pdA, pdB, s2_bits(0, 0));
+    // (every later step has stage 3; the next one's reads buffer 0, half 0)
+    step(YES, NO, NO, NO, NO, 0, 0, 0, 0, 0, 0, 0, 0, pre, sdA, sdB, pdB, pdA, ~0u);
+    step(YES, YES, NO, NO, YES, 0, 1, 0, 0, 0, 0, 0, 0, pre, sdB, sdA, pdA, pdB, s2_bits(0, 0));
     // The query tile of the chunk after next is loaded here, after the
     // step's last LDS read and unused until the next iteration: scalar loads
     // return out of order with LDS reads, so while one is in flight every
@@ -423,16 +443,19 @@ __global__ __launch_bounds__(T / 32 * 64, 1) void radial_bwd_dkdv_kernel(
       const bool more = c + 2 < nch;
       const int row_e = code_of(tile_d, c + 2);
       if (more) issue_half(c + 2, row_e, 0);
-      step(YES, YES, YES, bc, 0, bp, 1, bp, 0, sdA, sdB, pdB, pdA, s2_bits(bp, 1));
+      step(YES, YES, YES, YES, YES, bc, 0, bp, 1, bp, 0, bp, 1, pre, sdA, sdB, pdB, pdA,
+           s2_bits(bp, 1));
       if (more) issue_half(c + 2, row_e, 1);
-      step(YES, YES, YES, bc, 1, bc, 0, bp, 1, sdB, sdA, pdA, pdB, s2_bits(bc, 0));
+      step(YES, YES, YES, YES, YES, bc, 1, bc, 0, bp, 1, bc, 0, pre, sdB, sdA, pdA, pdB,
+           s2_bits(bc, 0));
       tile_d = tile_of(c + 3);
       chunk_end(c);
     }
     // drain: steps 2 nch, 2 nch + 1 (chunk nch - 1)
     const int bl = (nch - 1) % NB;
-    step(NO, YES, YES, 0, 0, bl, 1, bl, 0, sdA, sdB, pdB, pdA, s2_bits(bl, 1));
-    step(NO, NO, YES, 0, 0, 0, 0, bl, 1, sdB, sdA, pdA, pdB, ~0u);
+    step(NO, YES, YES, YES, YES, 0, 0, bl, 1, bl, 0, bl, 1, pre, sdA, sdB, pdB, pdA,
+         s2_bits(bl, 1));
+    step(NO, NO, YES, YES, NO, 0, 0, 0, 0, bl, 1, 0, 0, pre, sdB, sdA, pdA, pdB, ~0u);
   }
 
   if (k_ok) {
