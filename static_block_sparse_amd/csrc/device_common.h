@@ -79,14 +79,26 @@ __device__ __forceinline__ void st4(bf16 *p, bf16x4 v) {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Swizzled element offset of 16-byte block `ch` of row `row` in a row-major
-// [rows][D] bf16 LDS tile (no padding).  The block index is XORed with
-// f(row) = 2 * (row % H) + (row / H) % 2 (mod D/8, H = D/16): 16 consecutive
-// rows reading the same block, and the 4 rows x 2 blocks of a transposing
-// read, land in distinct bank groups.
+// [rows][D] bf16 LDS tile (no padding): the block index is XORed with f(row).
+// LDS has 64 banks of 4 bytes.  A 16-byte read serves 16 lanes per pass: at
+// D = 128 they read one block of 16 consecutive rows (256-byte rows, one bank
+// line each), at D = 64 one block of 16 rows two to a bank line.  A
+// transposing 8-byte read serves 32 lanes per pass, which read 4 consecutive
+// rows x 4 consecutive blocks (lane groups 0-15 and 16-31 take the two
+// 16-column halves of the same rows).  f is chosen so both kinds of pass
+// touch every bank once:
+//   D = 128: f = 4 (row % 4) + (row / 4) % 4 -- the 4 rows of a pass get
+//            XOR masks in distinct 4-block groups, and 16 consecutive rows
+//            get all 16 masks;
+//   D = 64:  f = 4 ((row / 2) % 2) + (row / 4) % 4 -- two rows share a bank
+//            line (one per half); the rows of a transposing pass that share
+//            a half get masks in distinct 4-block groups, and the 8 rows of
+//            one half among 16 consecutive rows get all 8 masks.
 template <int D>
 __device__ __forceinline__ int swz_f(int row) {
-  constexpr int NCH = D / 8, H = NCH / 2;
-  return (2 * (row % H) + (row / H) % 2) % NCH;
+  static_assert(D == 64 || D == 128, "head dim");
+  if constexpr (D == 128) return 4 * (row % 4) + (row / 4) % 4;
+  return 4 * ((row / 2) % 2) + (row / 4) % 4;
 }
 
 template <int D>
