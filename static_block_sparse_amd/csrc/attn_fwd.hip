@@ -68,6 +68,11 @@ struct FwdCfg {
   static_assert(NDMA >= 1 && CHUNK * 2 % (1024 * NW) == 0, "chunk must split evenly");
 };
 
+template <int V>
+struct FwdBuf {
+  static constexpr int value = V;
+};
+
 template <int D, int T, bool EXACT, bool PAIR>
 __global__ __launch_bounds__(T / 32 * 64 * (PAIR ? 2 : 1),
                              PAIR ? 256 / (T / 32 * 64) : 2) void radial_fwd_kernel(
@@ -166,12 +171,33 @@ __global__ __launch_bounds__(T / 32 * 64 * (PAIR ? 2 : 1),
   __syncthreads();
   const BandCtx bctx = make_band_ctx(mg, lds_rtab);
 
-  // lane (g, c32) in transposing-read group G = lane / 16 addresses row
-  // n0 + j / 4 and columns d0 + 4 (j % 4), j = lane % 16
-  const int j = lane & 15, G = lane >> 4;
+  // Per-lane LDS offsets of the operand reads, the same for both buffers and
+  // every 16-row step (the swizzle depends on the row modulo 16 only):
+  //   kof[kk]: S product, key row c32, 16-byte column block 2 kk + g (ld8)
+  //   vof[db][h]: the transposing V reads of column block db, rows r0 and
+  //   r0 + 8 of a 16-row step; lane (g, c32) in group G = lane / 16 addresses
+  //   row r0 = 4 (G / 2) + j / 4 and columns 32 db + 16 (G % 2) + 4 (j % 4),
+  //   j = lane % 16
+  // With the chunk loop unrolled over the two buffers, every read is one of
+  // these registers plus an immediate offset.
+  int kof[C::NKK], vof[C::NDB][2];
+#pragma unroll
+  for (int kk = 0; kk < C::NKK; ++kk) kof[kk] = swz<D>(c32, 2 * kk + g);
+  {
+    const int j = lane & 15, G = lane >> 4;
+    const int r0 = 4 * (G >> 1) + (j >> 2);
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db) {
+      const int col = db * 32 + 16 * (G & 1) + 4 * (j & 3);
+      vof[db][0] = swz<D>(r0, col >> 3) + (col & 7);
+      vof[db][1] = swz<D>(r0 + 8, col >> 3) + (col & 7);
+    }
+  }
 
-  for (int c = 0; c < nchunks; ++c) {
-    const bf16 *Ks = lds + (c & 1) * C::BUF;
+  // chunk c from buffer BS (0 or 1, = c % 2)
+  auto chunk = [&](int c, auto BS) __attribute__((always_inline)) {
+    constexpr int bsel = decltype(BS)::value;
+    const bf16 *Ks = lds + bsel * C::BUF;
     const bf16 *Vs = Ks + C::KC * D;
     const int raw = raw_next;
     const int key0 = key_of(raw, c);
@@ -180,7 +206,7 @@ __global__ __launch_bounds__(T / 32 * 64 * (PAIR ? 2 : 1),
     const bool partial = EXACT && (PAIR ? ((raw >> (29 + sub)) & 1) != 0 : raw < 0);
     raw_next = raw_after;
     // the next chunk's copy lands in the other buffer during these products
-    if (c + 1 < nchunks) issue_copy((c + 1) & 1, key_of(raw_next, c + 1));
+    if (c + 1 < nchunks) issue_copy(1 - bsel, key_of(raw_next, c + 1));
     if (c + 2 < nchunks) raw_after = chunk_raw(c + 2);
 
     if (member) {
@@ -193,7 +219,7 @@ __global__ __launch_bounds__(T / 32 * 64 * (PAIR ? 2 : 1),
       for (int kk = 0; kk < C::NKK; ++kk)
 #pragma unroll
         for (int kb = 0; kb < C::NKB; ++kb)
-          kf[kb][kk] = ld8(Ks + swz<D>(kb * 32 + c32, 2 * kk + g));
+          kf[kb][kk] = ld8(Ks + kb * 32 * D + kof[kk]);
 #pragma unroll
       for (int kb = 0; kb < C::NKB; ++kb) s[kb] = zero16();
 #pragma unroll
@@ -263,10 +289,9 @@ __global__ __launch_bounds__(T / 32 * 64 * (PAIR ? 2 : 1),
         for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
           for (int db = 0; db < C::NDB; ++db) {
-            const int col = db * 32 + 16 * (G & 1) + 4 * (j & 3);
-            const int n0 = kb * 32 + ks * 16 + 4 * (G >> 1) + (j >> 2);
-            const bf16x4 lo = ld_tr(Vs + swz<D>(n0, col >> 3) + (col & 7));
-            const bf16x4 hi = ld_tr(Vs + swz<D>(n0 + 8, col >> 3) + (col & 7));
+            const bf16 *vs = Vs + (kb * 32 + ks * 16) * D;
+            const bf16x4 lo = ld_tr(vs + vof[db][0]);
+            const bf16x4 hi = ld_tr(vs + vof[db][1]);
             oacc[db] = mfma32(cat(lo, hi), pf[kb][ks], oacc[db]);
           }
         }
@@ -284,6 +309,10 @@ __global__ __launch_bounds__(T / 32 * 64 * (PAIR ? 2 : 1),
 
     wait_vmem();      // this wave's copies of chunk c + 1 have landed
     __syncthreads();  // ... everyone's, and chunk c is no longer read
+  };
+  for (int c = 0; c < nchunks; c += 2) {
+    chunk(c, FwdBuf<0>{});
+    if (c + 1 < nchunks) chunk(c + 1, FwdBuf<1>{});
   }
 
   const float l_tot = pair_sum(l_run);
