@@ -485,6 +485,22 @@ __global__ __launch_bounds__(T / 32 * 64, 1) void radial_bwd_dkdv_kernel(
 //    buffered: S^T = K Q^T and dP^T = V dO^T read K and V row-major, and
 //    dQ^T += K^T dS^T reads K^T with transposing loads.
 // ---------------------------------------------------------------------------
+// Scheduling order for a run of NP matrix products whose operands come from
+// LDS reads, RPP reads per product: the first RA reads, then each product
+// followed by the reads of the product RA / RPP places later (group ID as
+// __builtin_amdgcn_sched_group_barrier).
+template <int ID, int RA, int NP, int RPP>
+__device__ __forceinline__ void read_ahead_order() {
+  static_assert(RA % RPP == 0 && RA / RPP <= NP, "read-ahead");
+  __builtin_amdgcn_sched_group_barrier(0x100, RA, ID);  // DS reads
+#pragma unroll
+  for (int i = 0; i < NP - RA / RPP; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, ID);  // one product
+    __builtin_amdgcn_sched_group_barrier(0x100, RPP, ID);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, RA / RPP, ID);
+}
+
 template <int D, int T, bool PAIR>
 struct DqCfg {
   static constexpr int NWR = T / 32;                // waves per query tile
@@ -560,13 +576,36 @@ __global__ __launch_bounds__(T / 32 * 64 * (PAIR ? 2 : 1),
   int rtab_v = 0;
   if constexpr (EXACT) rtab_v = threadIdx.x < 64 ? mg.band_rtab[threadIdx.x] : 0;
 
+  // Copies issued from inline assembly (copy_async): the compiler adds no
+  // wait of its own before the transposing K reads, which it cannot prove
+  // disjoint from the other buffer; the waits are the explicit ones below.
   typename C::Copier cp;
   cp.init(wave, lane);
-  auto issue = [&](int c, int k0) {
-    bf16 *kd = lds + (c & 1) * 2 * C::CHUNK;
-    cp.copy(kd, Kb + (int64_t)k0 * D, N - k0, wave);
-    cp.copy(kd + C::CHUNK, Vb + (int64_t)k0 * D, N - k0, wave);
+  auto issue = [&](int buf, int k0) {
+    bf16 *kd = lds + buf * 2 * C::CHUNK;
+    cp.copy_async(kd, Kb + (int64_t)k0 * D, N - k0, wave);
+    cp.copy_async(kd + C::CHUNK, Vb + (int64_t)k0 * D, N - k0, wave);
   };
+
+  // Per-lane LDS offsets, the same for both buffers and every 16-row step
+  // (the swizzle depends on the row modulo 16 only):
+  //   kof[kk]: S and dP products, key row c32, 16-byte block 2 kk + g
+  //   tof[db][h]: transposing K reads of column block db, rows r0 + 8 h
+  // With the chunk loop unrolled over the two buffers, every LDS read is one
+  // of these registers plus an immediate offset.
+  int kof[C::NKK], tof[C::NDB][2];
+#pragma unroll
+  for (int kk = 0; kk < C::NKK; ++kk) kof[kk] = swz<D>(c32, 2 * kk + g);
+  {
+    const int j = lane & 15, G = lane >> 4;
+    const int r0 = 4 * (G >> 1) + (j >> 2);
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db) {
+      const int col = db * 32 + 16 * (G & 1) + 4 * (j & 3);
+      tof[db][0] = swz<D>(r0, col >> 3) + (col & 7);
+      tof[db][1] = swz<D>(r0 + 8, col >> 3) + (col & 7);
+    }
+  }
 
   int raw_n = nch > 0 ? chunk_raw(0) : 0;   // list entries of chunks c and c + 1
   int raw_nn = nch > 1 ? chunk_raw(1) : 0;
@@ -578,14 +617,16 @@ __global__ __launch_bounds__(T / 32 * 64 * (PAIR ? 2 : 1),
   __syncthreads();
   const BandCtx bctx = make_band_ctx(mg, lds_rtab);
 
-  for (int c = 0; c < nch; ++c) {
+  // chunk c from buffer BS (= c % 2)
+  auto chunk = [&](int c, auto BS) __attribute__((always_inline)) {
+    constexpr int bsel = decltype(BS)::value;
     const int key0 = key_of(raw_n, c);
     // this wave's tile takes part in the chunk (always without PAIR)
     const bool member = PAIR ? ((raw_n >> (27 + sub)) & 1) != 0 : true;
     const bool partial = EXACT && (PAIR ? ((raw_n >> (29 + sub)) & 1) != 0 : raw_n < 0);
-    if (c + 1 < nch) issue(c + 1, key_of(raw_nn, c + 1));  // lands during this chunk
+    if (c + 1 < nch) issue(1 - bsel, key_of(raw_nn, c + 1));  // lands during this chunk
     const int raw_3 = c + 2 < nch ? chunk_raw(c + 2) : 0;
-    const bf16 *Ks = lds + (c & 1) * 2 * C::CHUNK;
+    const bf16 *Ks = lds + bsel * 2 * C::CHUNK;
     const bf16 *Vs = Ks + C::CHUNK;
 
     if (member) {
@@ -599,8 +640,8 @@ __global__ __launch_bounds__(T / 32 * 64 * (PAIR ? 2 : 1),
         bf16x8 ka[C::NKK], va[C::NKK];
 #pragma unroll
         for (int kk = 0; kk < C::NKK; ++kk) {
-          ka[kk] = ld8(Ks + swz<D>(kb * 32 + c32, 2 * kk + g));
-          va[kk] = ld8(Vs + swz<D>(kb * 32 + c32, 2 * kk + g));
+          ka[kk] = ld8(Ks + kb * 32 * D + kof[kk]);
+          va[kk] = ld8(Vs + kb * 32 * D + kof[kk]);
         }
         // dP starts from -Delta, so the products give dP - Delta directly
         f32x16 s = zero16(), dp;
@@ -611,6 +652,12 @@ __global__ __launch_bounds__(T / 32 * 64 * (PAIR ? 2 : 1),
           s = mfma32(ka[kk], qf[kk], s);
           dp = mfma32(va[kk], dof[kk], dp);
         }
+        // reads run four operands ahead of the products (left to itself the
+        // compiler issues each read right before its product and waits)
+        if (kb == 0)
+          read_ahead_order<1, 4, 2 * C::NKK, 1>();
+        else
+          read_ahead_order<3, 4, 2 * C::NKK, 1>();
         // register r holds key kb*32 + 8*(r/4) + 4g + r%4 of the chunk
         if (masked) {
 #pragma unroll
@@ -623,12 +670,19 @@ __global__ __launch_bounds__(T / 32 * 64 * (PAIR ? 2 : 1),
           const float p = fast_exp2(fmaf(s[r], scale_log2, nl2));
           dsb[r >> 3][r & 7] = bf16(p * dp[r]);
         }
-        // consecutive products share their dS operand (less switching)
+        // consecutive products share their dS operand (less switching); two
+        // operands (four transposing reads) ahead
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
           for (int db = 0; db < C::NDB; ++db)
-            adq[db] = mfma32(ld_trA<D>(Ks, db, kb, ks, lane), dsb[ks], adq[db]);
+            adq[db] = mfma32(cat(ld_tr(Ks + (kb * 32 + ks * 16) * D + tof[db][0]),
+                                 ld_tr(Ks + (kb * 32 + ks * 16) * D + tof[db][1])),
+                             dsb[ks], adq[db]);
+        if (kb == 0)
+          read_ahead_order<2, 4, 2 * C::NDB, 2>();
+        else
+          read_ahead_order<4, 4, 2 * C::NDB, 2>();
       }
     }  // member
 
@@ -636,6 +690,10 @@ __global__ __launch_bounds__(T / 32 * 64 * (PAIR ? 2 : 1),
     __syncthreads();  // ... and everywhere; chunk c is no longer read
     raw_n = raw_nn;
     raw_nn = raw_3;
+  };
+  for (int c = 0; c < nch; c += 2) {
+    chunk(c, BwdFlag<0>{});
+    if (c + 1 < nch) chunk(c + 1, BwdFlag<1>{});
   }
 
   if (q_ok) {
