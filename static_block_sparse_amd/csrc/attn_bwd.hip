@@ -108,9 +108,8 @@ struct DkdvCfg {
   static constexpr int NBUF = 4;         // chunk buffers
   static constexpr int CHUNK = MC * D;   // elements of one staged operand
   using Copier = TileCopier<D, MC, NW>;
-  static constexpr int LPW = MC / (4 * NW);  // lanes per wave copying row terms
   static constexpr int NCOPY = 2 * Copier::NDMA + 2;  // copies per wave per chunk
-  static_assert(NCOPY < 16 && LPW >= 1, "copy counts");
+  static_assert(NCOPY < 16, "copy counts");
 };
 
 template <int V>
@@ -194,23 +193,37 @@ __global__ __launch_bounds__(T / 32 * 64, 1) void radial_bwd_dkdv_kernel(
 
   typename C::Copier cp;
   cp.init(wave, lane);
-  // copies of chunk c (first row m0) into buffer c % NB; issued from inline
-  // assembly (see dma16_async), so every wait below is explicit
-  // (half 0: Q and the LSE terms; half 1: dO and the Delta terms)
-  auto issue_half = [&](int c, int code, int half) __attribute__((always_inline)) {
+  // Copies of chunk c (first row m0) into buffer c % NB, issued from inline
+  // assembly (see dma16_async), so every wait below is explicit.  Half 0 is
+  // Q and the LSE terms, half 1 dO and the Delta terms; each half is
+  // NDMA + 1 pieces per wave: piece 0 the MC row terms (every wave copies
+  // all of them, 4 bytes a lane, the same values to the same LDS words, so
+  // no lane mask is needed), pieces 1 .. NDMA the wave's share of the rows.
+  // The pieces are spread over a pipeline step's product slots.
+  static_assert(C::MC == 64, "row terms: one 4-byte copy per lane");
+  constexpr int NPIECE = C::Copier::NDMA + 1;
+  auto copy_piece = [&](int c, int code, int half, int k) __attribute__((always_inline)) {
     const int buf = c % NB;
     const int m0 = code & 0x7fffffff;
-    if (EXACT && half == 0 && tid == 0) lds_meta[buf] = code;
-    bf16 *qd = (half ? lds_do : lds_q) + buf * C::CHUNK;
-    cp.copy_async(qd, (half ? dOb : Qb) + (int64_t)m0 * D, N - m0, wave);
-    // row terms: wave w copies floats [w * 4 LPW, (w + 1) * 4 LPW) of each
-    float *rd = lds_r + buf * 2 * C::MC + half * C::MC + wave * 4 * C::LPW;
-    const u32x4 rl = rsrc_words((half ? NDelta : NLse2) + rbase + m0, (N - m0) * 4);
-    if (lane < C::LPW) dma16b_async(rl, rd, (wave * 4 * C::LPW + 4 * lane) * 4);
+    if (k == 0) {
+      const u32x4 rl = rsrc_words((half ? NDelta : NLse2) + rbase + m0, (N - m0) * 4);
+      dma4_async(rl, lds_r + buf * 2 * C::MC + half * C::MC, 4 * lane);
+    } else {
+      const u32x4 rq = rsrc_words((half ? dOb : Qb) + (int64_t)m0 * D, (N - m0) * D * 2);
+      const int jj = k - 1;
+      dma16_async(rq, (half ? lds_do : lds_q) + buf * C::CHUNK + (wave * C::Copier::NDMA + jj) * 512,
+                  cp.off[jj]);
+    }
   };
-  auto issue = [&](int c, int m0) __attribute__((always_inline)) {
-    issue_half(c, m0, 0);
-    issue_half(c, m0, 1);
+  auto meta = [&](int c, int code) __attribute__((always_inline)) {
+    if (EXACT && tid == 0) lds_meta[c % NB] = code;
+  };
+  auto issue = [&](int c, int code) __attribute__((always_inline)) {
+    meta(c, code);
+#pragma unroll
+    for (int half = 0; half < 2; ++half)
+#pragma unroll
+      for (int k = 0; k < NPIECE; ++k) copy_piece(c, code, half, k);
   };
 
   // Per-lane LDS offsets of the operand reads, the same for every chunk
@@ -259,7 +272,7 @@ __global__ __launch_bounds__(T / 32 * 64, 1) void radial_bwd_dkdv_kernel(
   auto step = [&](auto F1, auto F2, auto F3, auto FP, auto FN, int b1, int m1, int b2, int m2,
                   int b3, int m3, int b3n, int m3n, bf16x8 (&pre)[RA], Blk &sd_new,
                   const Blk &sd_old, bf16x8 (&pd_new)[2][2], const bf16x8 (&pd_old)[2][2],
-                  unsigned okm) __attribute__((always_inline)) {
+                  unsigned okm, auto NCPc, auto &&cpy) __attribute__((always_inline)) {
     constexpr bool s1 = decltype(F1)::value, s2 = decltype(F2)::value,
                    s3 = decltype(F3)::value;
     constexpr bool from_pre = decltype(FP)::value, to_pre = decltype(FN)::value;
@@ -357,6 +370,11 @@ __global__ __launch_bounds__(T / 32 * 64, 1) void radial_bwd_dkdv_kernel(
       else if constexpr (to_pre)
         pre[i + RA - NSL] = frag_next(i + RA - NSL);
       product(i, fr[i]);
+      // copy pieces cpy(0 .. NCP - 1), evenly spread over the slots
+      if constexpr (decltype(NCPc)::value > 0) {
+        constexpr int NCP = decltype(NCPc)::value, ST = NSL / (NCP + 1);
+        if (i % ST == ST - 1 && i / ST < NCP) cpy(i / ST);
+      }
       if constexpr (s2) {
         // pairs [e0, e1) go with slot i
         if (i >= S0 && i < SEND) {
@@ -423,12 +441,17 @@ __global__ __launch_bounds__(T / 32 * 64, 1) void radial_bwd_dkdv_kernel(
   };
 
   bf16x8 pre[RA];  // first operands of the next step
+  const BwdFlag<0> NOCOPY;
+  const BwdFlag<NPIECE> PIECES;
+  auto no_copy = [](int) {};
   if (nch > 0) {
     // chunk iteration 0: steps 0 and 1
     if (nch > 2) issue(2, row_c);
     // (every later step has stage 3; the next one's reads buffer 0, half 0)
-    step(YES, NO, NO, NO, NO, 0, 0, 0, 0, 0, 0, 0, 0, pre, sdA, sdB, pdB, pdA, ~0u);
-    step(YES, YES, NO, NO, YES, 0, 1, 0, 0, 0, 0, 0, 0, pre, sdB, sdA, pdA, pdB, s2_bits(0, 0));
+    step(YES, NO, NO, NO, NO, 0, 0, 0, 0, 0, 0, 0, 0, pre, sdA, sdB, pdB, pdA, ~0u, NOCOPY,
+         no_copy);
+    step(YES, YES, NO, NO, YES, 0, 1, 0, 0, 0, 0, 0, 0, pre, sdB, sdA, pdA, pdB, s2_bits(0, 0),
+         NOCOPY, no_copy);
     // The query tile of the chunk after next is loaded here, after the
     // step's last LDS read and unused until the next iteration: scalar loads
     // return out of order with LDS reads, so while one is in flight every
@@ -436,26 +459,37 @@ __global__ __launch_bounds__(T / 32 * 64, 1) void radial_bwd_dkdv_kernel(
     int tile_d = tile_of(3);
     chunk_end(0);
     // chunk iterations 1 .. nch - 1: steps 2c and 2c + 1; the copies of
-    // chunk c + 2 go out in two halves, one per step (a single burst from
-    // every wave queues at the CU's address unit and stalls instruction issue)
+    // chunk c + 2 go out one half per step, their pieces spread over the
+    // step's product slots (a burst queues at the CU's address unit and
+    // stalls instruction issue)
+    // In the last two iterations (no chunk c + 2) the copies still go out,
+    // unconditionally so that no branch splits a step: they copy the last
+    // chunk again into buffer (c + 2) % NB, whose chunk c - 2 is done and
+    // which nothing reads afterwards.
     for (int c = 1; c < nch; ++c) {
       const int bc = c % NB, bp = (c + NB - 1) % NB;
       const bool more = c + 2 < nch;
-      const int row_e = code_of(tile_d, c + 2);
-      if (more) issue_half(c + 2, row_e, 0);
+      const int row_e = code_of(tile_d, more ? c + 2 : nch - 1);
+      if (more) meta(c + 2, row_e);
+      auto copy_q = [&](int k) __attribute__((always_inline)) {
+        copy_piece(c + 2, row_e, 0, k);
+      };
+      auto copy_do = [&](int k) __attribute__((always_inline)) {
+        copy_piece(c + 2, row_e, 1, k);
+      };
       step(YES, YES, YES, YES, YES, bc, 0, bp, 1, bp, 0, bp, 1, pre, sdA, sdB, pdB, pdA,
-           s2_bits(bp, 1));
-      if (more) issue_half(c + 2, row_e, 1);
+           s2_bits(bp, 1), PIECES, copy_q);
       step(YES, YES, YES, YES, YES, bc, 1, bc, 0, bp, 1, bc, 0, pre, sdB, sdA, pdA, pdB,
-           s2_bits(bc, 0));
+           s2_bits(bc, 0), PIECES, copy_do);
       tile_d = tile_of(c + 3);
       chunk_end(c);
     }
     // drain: steps 2 nch, 2 nch + 1 (chunk nch - 1)
     const int bl = (nch - 1) % NB;
     step(NO, YES, YES, YES, YES, 0, 0, bl, 1, bl, 0, bl, 1, pre, sdA, sdB, pdB, pdA,
-         s2_bits(bl, 1));
-    step(NO, NO, YES, YES, NO, 0, 0, 0, 0, bl, 1, 0, 0, pre, sdB, sdA, pdA, pdB, ~0u);
+         s2_bits(bl, 1), NOCOPY, no_copy);
+    step(NO, NO, YES, YES, NO, 0, 0, 0, 0, bl, 1, 0, 0, pre, sdB, sdA, pdA, pdB, ~0u, NOCOPY,
+         no_copy);
   }
 
   if (k_ok) {

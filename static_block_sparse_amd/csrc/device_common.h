@@ -200,6 +200,22 @@ __device__ __forceinline__ void dma16_async(u32x4 r, const bf16 *lds_block, int 
 // lane l writes element e = blk*512 + 8l, i.e. row e / D and physical 16-byte
 // block (e % D) / 8, which holds logical block (physical ^ swz_f(row)) of the
 // row.  Rows at or past `valid` read as zeros.
+// The 4-byte form of dma16_async: lane l writes LDS bytes [4 l, 4 l + 4) of
+// lds_block from byte offset byte_off of the resource.
+__device__ __forceinline__ void dma4_async(u32x4 r, const void *lds_block, int byte_off) {
+  const unsigned lds_addr = __builtin_amdgcn_readfirstlane(
+      (unsigned)(unsigned long)(__attribute__((address_space(3))) const void *)lds_block);
+  unsigned saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dword %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds_addr), "v"(byte_off), "s"(r));
+}
+
 // Byte-addressed dma16_async (non-bf16 LDS data such as fp32 row terms).
 __device__ __forceinline__ void dma16b_async(u32x4 r, const void *lds_block, int byte_off) {
   dma16_async(r, (const bf16 *)lds_block, byte_off);
