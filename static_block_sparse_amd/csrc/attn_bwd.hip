@@ -202,8 +202,7 @@ __global__ __launch_bounds__(T / 32 * 64, 1) void radial_bwd_dkdv_kernel(
   // The pieces are spread over a pipeline step's product slots.
   static_assert(C::MC == 64, "row terms: one 4-byte copy per lane");
   constexpr int NPIECE = C::Copier::NDMA + 1;
-  auto copy_piece = [&](int c, int code, int half, int k) __attribute__((always_inline)) {
-    const int buf = c % NB;
+  auto copy_piece = [&](int buf, int code, int half, int k) __attribute__((always_inline)) {
     const int m0 = code & 0x7fffffff;
     if (k == 0) {
       const u32x4 rl = rsrc_words((half ? NDelta : NLse2) + rbase + m0, (N - m0) * 4);
@@ -215,15 +214,15 @@ __global__ __launch_bounds__(T / 32 * 64, 1) void radial_bwd_dkdv_kernel(
                   cp.off[jj]);
     }
   };
-  auto meta = [&](int c, int code) __attribute__((always_inline)) {
-    if (EXACT && tid == 0) lds_meta[c % NB] = code;
+  auto meta = [&](int buf, int code) __attribute__((always_inline)) {
+    if (EXACT && tid == 0) lds_meta[buf] = code;
   };
   auto issue = [&](int c, int code) __attribute__((always_inline)) {
-    meta(c, code);
+    meta(c % NB, code);
 #pragma unroll
     for (int half = 0; half < 2; ++half)
 #pragma unroll
-      for (int k = 0; k < NPIECE; ++k) copy_piece(c, code, half, k);
+      for (int k = 0; k < NPIECE; ++k) copy_piece(c % NB, code, half, k);
   };
 
   // Per-lane LDS offsets of the operand reads, the same for every chunk
@@ -466,23 +465,28 @@ __global__ __launch_bounds__(T / 32 * 64, 1) void radial_bwd_dkdv_kernel(
     // unconditionally so that no branch splits a step: they copy the last
     // chunk again into buffer (c + 2) % NB, whose chunk c - 2 is done and
     // which nothing reads afterwards.
-    for (int c = 1; c < nch; ++c) {
-      const int bc = c % NB, bp = (c + NB - 1) % NB;
+    // The loop is unrolled over the NB buffers, so every buffer index is a
+    // constant and every LDS access a per-lane register plus an immediate.
+    static_assert(NB == 4, "unrolled over four buffers");
+    auto iteration = [&](int c, auto BC) __attribute__((always_inline)) {
+      constexpr int bc = decltype(BC)::value, bp = (bc + NB - 1) % NB, bn = (bc + 2) % NB;
       const bool more = c + 2 < nch;
       const int row_e = code_of(tile_d, more ? c + 2 : nch - 1);
-      if (more) meta(c + 2, row_e);
-      auto copy_q = [&](int k) __attribute__((always_inline)) {
-        copy_piece(c + 2, row_e, 0, k);
-      };
-      auto copy_do = [&](int k) __attribute__((always_inline)) {
-        copy_piece(c + 2, row_e, 1, k);
-      };
+      if (more) meta(bn, row_e);
+      auto copy_q = [&](int k) __attribute__((always_inline)) { copy_piece(bn, row_e, 0, k); };
+      auto copy_do = [&](int k) __attribute__((always_inline)) { copy_piece(bn, row_e, 1, k); };
       step(YES, YES, YES, YES, YES, bc, 0, bp, 1, bp, 0, bp, 1, pre, sdA, sdB, pdB, pdA,
            s2_bits(bp, 1), PIECES, copy_q);
       step(YES, YES, YES, YES, YES, bc, 1, bc, 0, bp, 1, bc, 0, pre, sdB, sdA, pdA, pdB,
            s2_bits(bc, 0), PIECES, copy_do);
       tile_d = tile_of(c + 3);
       chunk_end(c);
+    };
+    for (int c = 1; c < nch; c += NB) {
+      iteration(c, BwdFlag<1>{});
+      if (c + 1 < nch) iteration(c + 1, BwdFlag<2>{});
+      if (c + 2 < nch) iteration(c + 2, BwdFlag<3>{});
+      if (c + 3 < nch) iteration(c + 3, BwdFlag<0>{});
     }
     // drain: steps 2 nch, 2 nch + 1 (chunk nch - 1)
     const int bl = (nch - 1) % NB;
