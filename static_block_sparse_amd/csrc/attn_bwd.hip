@@ -138,7 +138,7 @@ __global__ __launch_bounds__(T / 32 * 64, 1) void radial_bwd_dkdv_kernel(
   __shared__ int lds_meta[NB];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c32 = lane & 31, g = lane >> 5;
   const int work = xcd_remap(blockIdx.x, n_work, RADIAL_BWD_XCD_BLOCK);
   const int bh = work / nb;
