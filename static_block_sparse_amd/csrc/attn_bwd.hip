@@ -229,8 +229,10 @@ __global__ __launch_bounds__(T / 32 * 64, 1) void radial_bwd_dkdv_kernel(
   // buffer, block half and k step: the swizzle term of a row depends on the
   // row modulo 16 only, and blocks start at multiples of 16 rows.
   //   soff[kk]: stage 1, row c32, 16-byte column block 2 kk + g (ld8)
-  //   toff[db][h]: stage 3, the transposing reads of ld_trA for column block
-  //                db, rows r and r + 8 of the first 16-row step
+  //   toff[db][h]: stage 3, the transposing reads for column block db
+  //                (lane (g, c32) in group G = lane / 16 addresses row
+  //                r0 + 8 h, r0 = 4 (G / 2) + j / 4, and columns
+  //                32 db + 16 (G % 2) + 4 (j % 4), j = lane % 16)
   int soff[C::NKK], toff[C::NDB][2];
 #pragma unroll
   for (int kk = 0; kk < C::NKK; ++kk) soff[kk] = swz<D>(c32, 2 * kk + g);

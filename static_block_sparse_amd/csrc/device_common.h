@@ -68,10 +68,6 @@ __device__ __forceinline__ bf16x8 ld8(const bf16 *p) {
   return *reinterpret_cast<const bf16x8 *>(p);
 }
 
-__device__ __forceinline__ void st8(bf16 *p, bf16x8 v) {
-  *reinterpret_cast<bf16x8 *>(p) = v;
-}
-
 __device__ __forceinline__ void st4(bf16 *p, bf16x4 v) {
   *reinterpret_cast<bf16x4 *>(p) = v;
 }
@@ -152,11 +148,6 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, bf16 *lds_block,
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)lds_block, 16, byte_off, 0, 0, 0);
 }
 
-// Byte-addressed variant for non-bf16 LDS data (e.g. fp32 row terms).
-__device__ __forceinline__ void dma16b(__amdgpu_buffer_rsrc_t r, void *lds_block, int byte_off) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)lds_block, 16, byte_off, 0, 0, 0);
-}
-
 typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
 
 // The four words of a raw buffer resource over `bytes` bytes at p, in
@@ -194,12 +185,6 @@ __device__ __forceinline__ void dma16_async(u32x4 r, const bf16 *lds_block, int 
       : "s"(lds_addr), "v"(byte_off), "s"(r));
 }
 
-// Copies a ROWS x D bf16 tile (row-major at `src`, `valid` rows before the
-// end of the sequence) into a row-major, swizzled LDS tile, NW waves sharing
-// the work: copy jj of wave w fills LDS bytes [(w*NDMA + jj) * 1024, +1024);
-// lane l writes element e = blk*512 + 8l, i.e. row e / D and physical 16-byte
-// block (e % D) / 8, which holds logical block (physical ^ swz_f(row)) of the
-// row.  Rows at or past `valid` read as zeros.
 // The 4-byte form of dma16_async: lane l writes LDS bytes [4 l, 4 l + 4) of
 // lds_block from byte offset byte_off of the resource.
 __device__ __forceinline__ void dma4_async(u32x4 r, const void *lds_block, int byte_off) {
@@ -216,39 +201,22 @@ __device__ __forceinline__ void dma4_async(u32x4 r, const void *lds_block, int b
       : "s"(lds_addr), "v"(byte_off), "s"(r));
 }
 
-// Byte-addressed dma16_async (non-bf16 LDS data such as fp32 row terms).
-__device__ __forceinline__ void dma16b_async(u32x4 r, const void *lds_block, int byte_off) {
-  dma16_async(r, (const bf16 *)lds_block, byte_off);
-}
-
+// Copies a ROWS x D bf16 tile (row-major at `src`, `valid` rows before the
+// end of the sequence) into a row-major, swizzled LDS tile, NW waves sharing
+// the work: copy jj of wave w fills LDS bytes [(w*NDMA + jj) * 1024, +1024);
+// lane l writes element e = blk*512 + 8l, i.e. row e / D and physical 16-byte
+// block (e % D) / 8, which holds logical block (physical ^ swz_f(row)) of the
+// row.  Rows at or past `valid` read as zeros.
 template <int D, int ROWS, int NW>
 struct TileCopier {
   static constexpr int NDMA = ROWS * D * 2 / 1024 / NW;  // copies per wave
   static_assert(NDMA >= 1 && ROWS * D * 2 % (1024 * NW) == 0, "tile split");
   int off[NDMA];
   __device__ __forceinline__ void init(int wave, int lane);
-  __device__ __forceinline__ void copy(bf16 *dst, const bf16 *src, int valid, int wave) const {
-    const auto r = make_rsrc(src, valid * D * 2);
-#pragma unroll
-    for (int jj = 0; jj < NDMA; ++jj) dma16(r, dst + (wave * NDMA + jj) * 512, off[jj]);
-  }
-  // the same copy issued with dma16_async (the caller waits with wait_vmem)
+  // issued with dma16_async (the caller waits with wait_vmem)
   __device__ __forceinline__ void copy_async(bf16 *dst, const bf16 *src, int valid,
                                              int wave) const;
 };
-
-// A operand (32 x 16) of a product contracting over the rows of a row-major
-// swizzled [rows][D] LDS tile, for output rows d = 32 db + (lane % 32) and
-// contraction rows 32 rb + 16 ks + (the permuted K assignment), read with
-// two transposing loads.
-template <int D>
-__device__ __forceinline__ bf16x8 ld_trA(const bf16 *tile, int db, int rb, int ks, int lane) {
-  const int j = lane & 15, G = lane >> 4;
-  const int col = db * 32 + 16 * (G & 1) + 4 * (j & 3);
-  const int r0 = rb * 32 + ks * 16 + 4 * (G >> 1) + (j >> 2);
-  return cat(ld_tr(tile + swz<D>(r0, col >> 3) + (col & 7)),
-             ld_tr(tile + swz<D>(r0 + 8, col >> 3) + (col & 7)));
-}
 
 // s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maximum)
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
@@ -435,61 +403,5 @@ __device__ __forceinline__ int xcd_remap(int b, int n, int blk) {
   return ((k / blk) * X + x) * blk + k % blk;
 }
 
-// Rows [0, ROWS) x cols [0, D) of a row-major bf16 tile into LDS with row
-// stride LS (elements); rows at or beyond `valid` are zero-filled.
-template <int ROWS, int D, int LS, int NT>
-__device__ __forceinline__ void load_rows(bf16 *lds, const bf16 *g, int valid, int tid) {
-  constexpr int CH = D / 8;           // 16-byte chunks per row
-  constexpr int TOT = ROWS * CH;
-  static_assert(TOT % NT == 0, "tile chunks must divide the thread count");
-  bf16x8 buf[TOT / NT];
-#pragma unroll
-  for (int it = 0; it < TOT / NT; ++it) {
-    const int c = tid + it * NT;
-    const int row = c / CH, ch = c % CH;
-    buf[it] = row < valid ? ld8(g + (int64_t)row * D + ch * 8) : zero_bf16x8();
-  }
-#pragma unroll
-  for (int it = 0; it < TOT / NT; ++it) {
-    const int c = tid + it * NT;
-    const int row = c / CH, ch = c % CH;
-    st8(lds + row * LS + ch * 8, buf[it]);
-  }
-}
-
-// Same tile stored transposed: lds[d * LS + row].  Each thread moves a
-// 4-row x 8-column block; consecutive threads take consecutive row groups so
-// the 8-byte LDS stores of a wave are contiguous.
-template <int ROWS, int D, int LS, int NT>
-__device__ __forceinline__ void load_rows_t(bf16 *lds, const bf16 *g, int valid, int tid) {
-  constexpr int RG = ROWS / 4;        // row groups
-  constexpr int TOT = RG * (D / 8);
-  static_assert(TOT % NT == 0, "tile blocks must divide the thread count");
-  bf16x8 buf[TOT / NT][4];
-#pragma unroll
-  for (int it = 0; it < TOT / NT; ++it) {
-    const int c = tid + it * NT;
-    const int rg = c % RG, ch = c / RG;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = rg * 4 + r;
-      buf[it][r] = row < valid ? ld8(g + (int64_t)row * D + ch * 8) : zero_bf16x8();
-    }
-  }
-#pragma unroll
-  for (int it = 0; it < TOT / NT; ++it) {
-    const int c = tid + it * NT;
-    const int rg = c % RG, ch = c / RG;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      bf16x4 col;
-      col[0] = buf[it][0][e];
-      col[1] = buf[it][1][e];
-      col[2] = buf[it][2][e];
-      col[3] = buf[it][3][e];
-      st4(lds + (ch * 8 + e) * LS + rg * 4, col);
-    }
-  }
-}
 
 }  // namespace radial
