@@ -61,6 +61,39 @@ def test_backward_small(f, s, T, D, B, H):
             check_close(f64(dv[b, h]), rv, f"dV b={b} h={h}", normalise=True)
 
 
+# Columns of 1 .. 9 query chunks (64 rows each): the dK/dV walk has a two-step
+# prologue, a loop unrolled over its four chunk buffers and a drain, so every
+# column length modulo 4 and the shortest columns take different paths.
+# (f, s, chunks per column): single-frame and two-frame layouts are dense.
+SHORT_COLUMNS = [(1, 20, 1), (1, 70, 2), (1, 130, 3), (1, 200, 4), (1, 260, 5), (1, 330, 6),
+                 (1, 390, 7), (2, 230, 8), (2, 260, 9)]
+
+
+@pytest.mark.parametrize("f,s,n_chunks", SHORT_COLUMNS)
+def test_backward_short_columns(f, s, n_chunks):
+    T, D = 128, 128
+    N = f * s
+    nb = (N + T - 1) // T
+    L = sba.Layout(f, s, T)
+    col_ptr, row_idx = L.csc()
+    col_ptr = np.asarray(col_ptr)
+    last = np.asarray(row_idx)[col_ptr[1:] - 1] & 0x7fffffff
+    chunks = (np.diff(col_ptr) * 2 - np.where(last == nb - 1, 2 - (N - (nb - 1) * T + 63) // 64, 0))
+    _say(f"[bwd short] f={f} s={s} chunks per column {sorted(set(chunks.tolist()))}")
+    assert set(chunks.tolist()) == {n_chunks}
+    scale = 1.0 / np.sqrt(D)
+    q, k, v, do = workloads.make_inputs(1, 1, N, D, 300 + s, with_dout=True)
+    qc, kc, vc, dc = q.cuda(), k.cuda(), v.cuda(), do.cuda()
+    o, lse = sba.attn_fwd(qc, kc, vc, L, scale)
+    dq, dk, dv = sba.attn_bwd(qc, kc, vc, o, lse, dc, L, scale)
+    torch.cuda.synchronize()
+    kept = om.kept_tiles(f, s, T, True)
+    rq, rk, rv = oa.bwd(f64(q[0, 0]), f64(k[0, 0]), f64(v[0, 0]), f64(do[0, 0]), kept, T, scale)
+    check_close(f64(dq[0, 0]), rq, "dQ", normalise=True)
+    check_close(f64(dk[0, 0]), rk, "dK", normalise=True)
+    check_close(f64(dv[0, 0]), rv, "dV", normalise=True)
+
+
 def test_backward_sink_off_and_peaky():
     f, s, T, D = 9, 200, 128, 128
     N = f * s
