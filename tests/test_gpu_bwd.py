@@ -15,7 +15,7 @@ import torch
 
 import static_block_sparse_amd as sba
 import workloads
-from gpu_util import PEAKY_REL_MAX, check_close, f64, sample_tiles
+from gpu_util import PEAKY_REL_MAX, check_close, check_lse, f64, sample_tiles
 from oracle import attention as oa
 from oracle import mask as om
 
@@ -88,6 +88,10 @@ def test_backward_short_columns(f, s, n_chunks):
     dq, dk, dv = sba.attn_bwd(qc, kc, vc, o, lse, dc, L, scale)
     torch.cuda.synchronize()
     kept = om.kept_tiles(f, s, T, True)
+    # the forward and dQ walk rows of the same lengths (loops unrolled by two)
+    ro, rl = oa.fwd(f64(q[0, 0]), f64(k[0, 0]), f64(v[0, 0]), kept, T, scale)
+    check_close(f64(o[0, 0]), ro, "O")
+    check_lse(f64(lse[0, 0]), rl, "LSE")
     rq, rk, rv = oa.bwd(f64(q[0, 0]), f64(k[0, 0]), f64(v[0, 0]), f64(do[0, 0]), kept, T, scale)
     check_close(f64(dq[0, 0]), rq, "dQ", normalise=True)
     check_close(f64(dk[0, 0]), rk, "dK", normalise=True)
