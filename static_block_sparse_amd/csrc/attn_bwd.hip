@@ -525,22 +525,6 @@ __global__ __launch_bounds__(T / 32 * 64, 1) void radial_bwd_dkdv_kernel(
 //    buffered: S^T = K Q^T and dP^T = V dO^T read K and V row-major, and
 //    dQ^T += K^T dS^T reads K^T with transposing loads.
 // ---------------------------------------------------------------------------
-// Scheduling order for a run of NP matrix products whose operands come from
-// LDS reads, RPP reads per product: the first RA reads, then each product
-// followed by the reads of the product RA / RPP places later (group ID as
-// __builtin_amdgcn_sched_group_barrier).
-template <int ID, int RA, int NP, int RPP>
-__device__ __forceinline__ void read_ahead_order() {
-  static_assert(RA % RPP == 0 && RA / RPP <= NP, "read-ahead");
-  __builtin_amdgcn_sched_group_barrier(0x100, RA, ID);  // DS reads
-#pragma unroll
-  for (int i = 0; i < NP - RA / RPP; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, ID);  // one product
-    __builtin_amdgcn_sched_group_barrier(0x100, RPP, ID);
-  }
-  __builtin_amdgcn_sched_group_barrier(0x008, RA / RPP, ID);
-}
-
 template <int D, int T, bool PAIR>
 struct DqCfg {
   static constexpr int NWR = T / 32;                // waves per query tile

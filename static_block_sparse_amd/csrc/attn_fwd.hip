@@ -210,9 +210,8 @@ __global__ __launch_bounds__(T / 32 * 64 * (PAIR ? 2 : 1),
     if (c + 2 < nchunks) raw_after = chunk_raw(c + 2);
 
     if (member) {
-      // S^T for the wave's 32 queries against the chunk's KC keys.  The K
-      // fragments of block kb + 1 are read while block kb's products run, so
-      // the LDS latency is paid once per chunk rather than once per product.
+      // S^T for the wave's 32 queries against the chunk's KC keys, the K
+      // fragments read four products ahead (products in the order kk, kb)
       f32x16 s[C::NKB];
       bf16x8 kf[C::NKB][C::NKK];
 #pragma unroll
@@ -226,13 +225,7 @@ __global__ __launch_bounds__(T / 32 * 64 * (PAIR ? 2 : 1),
       for (int kk = 0; kk < C::NKK; ++kk)
 #pragma unroll
         for (int kb = 0; kb < C::NKB; ++kb) s[kb] = mfma32(kf[kb][kk], qf[kk], s[kb]);
-      __builtin_amdgcn_sched_group_barrier(0x100, C::NKK, 1);  // block 0 reads
-#pragma unroll
-      for (int i = 0; i < C::NKK * (C::NKB - 1); ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);     // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);     // next block's read
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, C::NKK, 1);  // last block's MFMAs
+      read_ahead_order<1, 4, C::NKK * C::NKB, 1>();
       if (key0 + C::KC > N) {  // the tail chunk: keys at or past N get -inf
         // register r of block kb holds key key0 + kb*32 + 8*(r/4) + 4g + r%4
         const int lim = N - key0 - 4 * g;

@@ -218,6 +218,22 @@ struct TileCopier {
                                              int wave) const;
 };
 
+// Scheduling order for a run of NP matrix products whose operands come from
+// LDS reads, RPP reads per product: the first RA reads, then each product
+// followed by the reads of the product RA / RPP places later (group ID as
+// __builtin_amdgcn_sched_group_barrier).
+template <int ID, int RA, int NP, int RPP>
+__device__ __forceinline__ void read_ahead_order() {
+  static_assert(RA % RPP == 0 && RA / RPP <= NP, "read-ahead");
+  __builtin_amdgcn_sched_group_barrier(0x100, RA, ID);  // DS reads
+#pragma unroll
+  for (int i = 0; i < NP - RA / RPP; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, ID);  // one product
+    __builtin_amdgcn_sched_group_barrier(0x100, RPP, ID);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, RA / RPP, ID);
+}
+
 // s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maximum)
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
