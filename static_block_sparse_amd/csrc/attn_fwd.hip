@@ -28,13 +28,14 @@
 //  * the running max is only moved when a chunk's max exceeds it by more
 //    than 8 (log2 units); probabilities then stay below 2^8, exact in the
 //    final O / l and LSE, and the O rescale is skipped on most chunks.
-//  * pairs (PAIR, the default): a workgroup of 2 T / 32 waves takes the
-//    adjacent query tiles 2p and 2p + 1 and walks the sorted union of their
-//    key tiles (built by the mask compiler).  Every staged chunk then serves
-//    both tiles' waves, which halves the global -> LDS copies per product;
+//  * query-tile groups: a workgroup of G T / 32 waves takes G adjacent
+//    query tiles (G = 3, three waves per SIMD; pairs or single tiles only
+//    when the mask compiler built no triple lists) and walks the sorted
+//    union of their key tiles.  Every staged chunk then serves G tiles'
+//    waves, which divides the global -> LDS copies per product by about G;
 //    at the power cap the copies' energy is a large share of the budget.
-//    A wave skips the chunks of key tiles its own tile does not keep (5-15%
-//    of the walk for the radial mask).
+//    A wave skips the chunks of key tiles its own tile does not keep (6% of
+//    a pair's walk, 12% of a triple's, for the radial mask at 720p).
 //  * token-exact layouts (EXACT): in the chunks of tiles marked partial,
 //    each lane masks the keys outside its query's allowed runs (one per key
 //    frame the chunk touches, however many) before the max.
@@ -43,19 +44,16 @@
 #include "device_common.h"
 #include "kernels.h"
 
-#ifndef RADIAL_FWD_PAIR
-#define RADIAL_FWD_PAIR 1  // query tiles processed in pairs sharing K/V chunks
-#endif
 #ifndef RADIAL_FWD_XCD_BLOCK
 #define RADIAL_FWD_XCD_BLOCK 16  // work items per XCD block (see xcd_remap)
 #endif
 
 namespace radial {
 
-template <int D, int T, bool PAIR>
+template <int D, int T, int G>
 struct FwdCfg {
   static constexpr int NWR = T / 32;    // waves per query tile
-  static constexpr int NW = NWR * (PAIR ? 2 : 1);  // waves per workgroup
+  static constexpr int NW = NWR * G;    // waves per workgroup
   static constexpr int NT = NW * 64;    // threads per workgroup
   static constexpr int KC = 64;         // keys per pipeline chunk
   static constexpr int CPT = T / KC;    // chunks per tile
@@ -64,8 +62,12 @@ struct FwdCfg {
   static constexpr int NKK = D / 16;    // K steps of the Q K^T product
   static constexpr int CHUNK = KC * D;  // elements of one staged operand
   static constexpr int BUF = 2 * CHUNK; // elements per buffer (K then V)
-  static constexpr int NDMA = CHUNK * 2 / 1024 / NW;  // 1 KB copies per wave per operand
-  static_assert(NDMA >= 1 && CHUNK * 2 % (1024 * NW) == 0, "chunk must split evenly");
+  static constexpr int NKB1 = CHUNK * 2 / 1024;       // 1 KB copies per operand
+  // copying waves: the largest power of two up to NW (all waves for single
+  // tiles and pairs; 8 of the 12 for triples of 128-row tiles)
+  static constexpr int NCW = NW >= 16 ? 16 : NW >= 8 ? 8 : NW >= 4 ? 4 : NW >= 2 ? 2 : 1;
+  static constexpr int NDMA = NKB1 / NCW;             // 1 KB copies per copying wave
+  static_assert(NDMA >= 1 && NKB1 % NCW == 0, "chunk must split evenly");
 };
 
 template <int V>
@@ -73,30 +75,38 @@ struct FwdBuf {
   static constexpr int value = V;
 };
 
-template <int D, int T, bool EXACT, bool PAIR>
-__global__ __launch_bounds__(T / 32 * 64 * (PAIR ? 2 : 1),
-                             PAIR ? 256 / (T / 32 * 64) : 2) void radial_fwd_kernel(
-    const bf16 *__restrict__ Q, const bf16 *__restrict__ K, const bf16 *__restrict__ V,
-    bf16 *__restrict__ O, float *__restrict__ LSE, const int32_t *__restrict__ row_ptr,
-    const int32_t *__restrict__ col_idx, const int32_t *__restrict__ pair_ptr,
-    const int32_t *__restrict__ pair_idx, int32_t N, int32_t nb, int32_t n_work,
-    float scale_log2, MaskGeom mg) {
-  using C = FwdCfg<D, T, PAIR>;
+// Query-tile group lists: tile-index mask and the shifts of a row's
+// membership and partial bits (G = 1 reads the CSR rows, partial = bit 31).
+template <int G>
+struct GroupBits {
+  static constexpr int32_t kTile = G == 3 ? kTriTile : G == 2 ? kPairTile : 0x7fffffff;
+  static constexpr int kIn = G == 3 ? 25 : 27, kPart = G == 3 ? 28 : 29;
+};
+
+template <int D, int T, bool EXACT, int G>
+__global__ __launch_bounds__(T / 32 * 64 * G, G > 1 ? 256 / (T / 32 * 64) : 2) void
+radial_fwd_kernel(const bf16 *__restrict__ Q, const bf16 *__restrict__ K,
+                  const bf16 *__restrict__ V, bf16 *__restrict__ O, float *__restrict__ LSE,
+                  const int32_t *__restrict__ row_ptr, const int32_t *__restrict__ col_idx,
+                  const int32_t *__restrict__ grp_ptr, const int32_t *__restrict__ grp_idx,
+                  int32_t N, int32_t nb, int32_t n_work, float scale_log2, MaskGeom mg) {
+  using C = FwdCfg<D, T, G>;
+  using GB = GroupBits<G>;
   constexpr float kSlack = 8.f;  // lazy-rescale threshold (log2 units)
   __shared__ __attribute__((aligned(1024))) bf16 lds[2 * C::BUF];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c32 = lane & 31, g = lane >> 5;
-  // work item: one query tile, or with PAIR the query tiles 2p (waves
-  // [0, NWR)) and 2p + 1 (waves [NWR, 2 NWR)) over the union of their key
-  // tiles, so every staged K/V chunk serves twice the queries
-  const int nwork_head = PAIR ? (nb + 1) / 2 : nb;
+  // work item: G query tiles G p + k (waves [k NWR, (k + 1) NWR)) over the
+  // union of their key tiles, so every staged K/V chunk serves G times the
+  // queries
+  const int nwork_head = (nb + G - 1) / G;
   const int work = xcd_remap(blockIdx.x, n_work, RADIAL_FWD_XCD_BLOCK);
   const int bh = work / nwork_head;
   const int wi = work - bh * nwork_head;
-  const int sub = PAIR ? wave / C::NWR : 0;  // which tile of the pair
-  const int u = PAIR ? 2 * wi + sub : wi;
+  const int sub = G > 1 ? wave / C::NWR : 0;  // which tile of the group
+  const int u = G * wi + sub;
   const int64_t base = (int64_t)bh * N * D;
   const bf16 *Kb = K + base;
   const bf16 *Vb = V + base;
@@ -116,9 +126,9 @@ __global__ __launch_bounds__(T / 32 * 64 * (PAIR ? 2 : 1),
   // chunks of the last key tile that lie entirely at or beyond N.  A list
   // entry is a key tile (CSR: bit 31 marks a partial tile; pair lists:
   // membership and partial bits per tile of the pair, see kernels.h).
-  const int32_t *lptr = PAIR ? pair_ptr : row_ptr;
-  const int32_t *lidx = PAIR ? pair_idx : col_idx;
-  constexpr int32_t TMASK = PAIR ? kPairTile : 0x7fffffff;
+  const int32_t *lptr = G > 1 ? grp_ptr : row_ptr;
+  const int32_t *lidx = G > 1 ? grp_idx : col_idx;
+  constexpr int32_t TMASK = GB::kTile;
   const int t_begin = lptr[wi], t_end = lptr[wi + 1];
   int nchunks = (t_end - t_begin) * C::CPT;
   if (t_end > t_begin && (lidx[t_end - 1] & TMASK) == nb - 1)
@@ -131,18 +141,21 @@ __global__ __launch_bounds__(T / 32 * 64 * (PAIR ? 2 : 1),
   const int qi = qrow / mg.s, qa = qrow - (qrow / mg.s) * mg.s;
 
   // Chunk staging by direct global -> LDS copies (no staging registers):
-  // copy jj of this wave fills LDS bytes [(wave*NDMA + jj) * 1024, +1024) of
-  // an operand; lane l writes element e = blk*512 + 8l, i.e. row e / D and
-  // physical 16-byte block (e % D) / 8, which holds logical block
-  // physical ^ swz_f(row) of that row.  Lanes past N write zeros.
+  // copy jj of copying wave w (w < NCW) fills LDS bytes
+  // [(w*NDMA + jj) * 1024, +1024) of an operand; lane l writes element
+  // e = blk*512 + 8l, i.e. row e / D and physical 16-byte block (e % D) / 8,
+  // which holds logical block physical ^ swz_f(row) of that row.  Lanes past
+  // N write zeros.
+  const bool copier = wave < C::NCW;
   int dma_off[C::NDMA];
 #pragma unroll
   for (int jj = 0; jj < C::NDMA; ++jj) {
-    const int e = (wave * C::NDMA + jj) * 512 + 8 * lane;
+    const int e = ((wave % C::NCW) * C::NDMA + jj) * 512 + 8 * lane;
     const int row = e / D, pblk = (e % D) / 8;
     dma_off[jj] = row * D * 2 + 16 * (pblk ^ swz_f<D>(row));
   }
   auto issue_copy = [&](int buf, int k0) {
+    if (!copier) return;
     const int bytes = (N - k0) * D * 2;
     const auto rk = make_rsrc(Kb + (int64_t)k0 * D, bytes);
     const auto rv = make_rsrc(Vb + (int64_t)k0 * D, bytes);
@@ -175,8 +188,8 @@ __global__ __launch_bounds__(T / 32 * 64 * (PAIR ? 2 : 1),
   // every 16-row step (the swizzle depends on the row modulo 16 only):
   //   kof[kk]: S product, key row c32, 16-byte column block 2 kk + g (ld8)
   //   vof[db][h]: the transposing V reads of column block db, rows r0 and
-  //   r0 + 8 of a 16-row step; lane (g, c32) in group G = lane / 16 addresses
-  //   row r0 = 4 (G / 2) + j / 4 and columns 32 db + 16 (G % 2) + 4 (j % 4),
+  //   r0 + 8 of a 16-row step; lane (g, c32) in lane group lg = lane / 16
+  //   addresses row r0 = 4 (lg / 2) + j / 4 and columns 32 db + 16 (lg % 2) + 4 (j % 4),
   //   j = lane % 16
   // With the chunk loop unrolled over the two buffers, every read is one of
   // these registers plus an immediate offset.
@@ -184,11 +197,11 @@ __global__ __launch_bounds__(T / 32 * 64 * (PAIR ? 2 : 1),
 #pragma unroll
   for (int kk = 0; kk < C::NKK; ++kk) kof[kk] = swz<D>(c32, 2 * kk + g);
   {
-    const int j = lane & 15, G = lane >> 4;
-    const int r0 = 4 * (G >> 1) + (j >> 2);
+    const int j = lane & 15, lg = lane >> 4;
+    const int r0 = 4 * (lg >> 1) + (j >> 2);
 #pragma unroll
     for (int db = 0; db < C::NDB; ++db) {
-      const int col = db * 32 + 16 * (G & 1) + 4 * (j & 3);
+      const int col = db * 32 + 16 * (lg & 1) + 4 * (j & 3);
       vof[db][0] = swz<D>(r0, col >> 3) + (col & 7);
       vof[db][1] = swz<D>(r0 + 8, col >> 3) + (col & 7);
     }
@@ -201,9 +214,9 @@ __global__ __launch_bounds__(T / 32 * 64 * (PAIR ? 2 : 1),
     const bf16 *Vs = Ks + C::KC * D;
     const int raw = raw_next;
     const int key0 = key_of(raw, c);
-    // this wave's tile takes part in the chunk (always without PAIR)
-    const bool member = PAIR ? ((raw >> (27 + sub)) & 1) != 0 : true;
-    const bool partial = EXACT && (PAIR ? ((raw >> (29 + sub)) & 1) != 0 : raw < 0);
+    // this wave's tile takes part in the chunk (always for single tiles)
+    const bool member = G > 1 ? ((raw >> (GB::kIn + sub)) & 1) != 0 : true;
+    const bool partial = EXACT && (G > 1 ? ((raw >> (GB::kPart + sub)) & 1) != 0 : raw < 0);
     raw_next = raw_after;
     // the next chunk's copy lands in the other buffer during these products
     if (c + 1 < nchunks) issue_copy(1 - bsel, key_of(raw_next, c + 1));
@@ -326,24 +339,30 @@ __global__ __launch_bounds__(T / 32 * 64 * (PAIR ? 2 : 1),
   }
 }
 
-template <int D, int T, bool EXACT, bool PAIR>
+template <int D, int T, bool EXACT, int G>
 hipError_t launch_fwd_t(const FwdArgs &a, hipStream_t stream) {
-  const int64_t works = (int64_t)a.BH * (PAIR ? (a.nb + 1) / 2 : a.nb);
-  hipLaunchKernelGGL((radial_fwd_kernel<D, T, EXACT, PAIR>), dim3((unsigned)works),
-                     dim3(FwdCfg<D, T, PAIR>::NT), 0, stream, (const bf16 *)a.q,
+  const int64_t works = (int64_t)a.BH * ((a.nb + G - 1) / G);
+  hipLaunchKernelGGL((radial_fwd_kernel<D, T, EXACT, G>), dim3((unsigned)works),
+                     dim3(FwdCfg<D, T, G>::NT), 0, stream, (const bf16 *)a.q,
                      (const bf16 *)a.k, (const bf16 *)a.v, (bf16 *)a.o, a.lse, a.row_ptr,
-                     a.col_idx, a.pair_ptr, a.pair_idx, a.N, a.nb, (int32_t)works,
+                     a.col_idx, G == 3 ? a.tri_ptr : a.pair_ptr,
+                     G == 3 ? a.tri_idx : a.pair_idx, a.N, a.nb, (int32_t)works,
                      a.scale * kLog2e, a.mask);
   return hipGetLastError();
 }
 
+// Query tiles in triples, else in pairs, else single, as far as the layout
+// has the group lists and max_group allows.
+template <int D, int T, bool EXACT>
+hipError_t launch_fwd_g(const FwdArgs &a, hipStream_t stream) {
+  if (a.max_group >= 3 && a.tri_ptr) return launch_fwd_t<D, T, EXACT, 3>(a, stream);
+  if (a.max_group >= 2 && a.pair_ptr) return launch_fwd_t<D, T, EXACT, 2>(a, stream);
+  return launch_fwd_t<D, T, EXACT, 1>(a, stream);
+}
+
 template <int D, int T>
 hipError_t launch_fwd_t(const FwdArgs &a, hipStream_t stream) {
-  if (RADIAL_FWD_PAIR && a.pair_ptr)
-    return a.mask.exact ? launch_fwd_t<D, T, true, true>(a, stream)
-                        : launch_fwd_t<D, T, false, true>(a, stream);
-  return a.mask.exact ? launch_fwd_t<D, T, true, false>(a, stream)
-                      : launch_fwd_t<D, T, false, false>(a, stream);
+  return a.mask.exact ? launch_fwd_g<D, T, true>(a, stream) : launch_fwd_g<D, T, false>(a, stream);
 }
 
 hipError_t launch_fwd(const FwdArgs &a, hipStream_t stream) {

@@ -32,6 +32,14 @@ bool forced_alloc_failure() {
   return e && e[0] == '1';
 }
 
+// Query-tile grouping hook for tests: RADIAL_TEST_FWD_GROUP=1 or 2 caps the
+// forward's grouping (single tiles / pairs) so a test can compare the three
+// forms, which must agree bit for bit.  Unset: up to triples.
+int32_t forced_max_group() {
+  const char *e = std::getenv("RADIAL_TEST_FWD_GROUP");
+  return (e && (e[0] == '1' || e[0] == '2') && e[1] == 0) ? e[0] - '0' : 3;
+}
+
 void free_device(radial_layout *L) {
   if (L->d_base) {
     int cur = -1;
@@ -42,7 +50,7 @@ void free_device(radial_layout *L) {
   }
   L->d_base = nullptr;
   L->d_row_ptr = L->d_col_idx = L->d_col_ptr = L->d_row_idx = L->d_col_order = nullptr;
-  L->d_band_rtab = L->d_pair_ptr = L->d_pair_idx = nullptr;
+  L->d_band_rtab = L->d_pair_ptr = L->d_pair_idx = L->d_tri_ptr = L->d_tri_idx = nullptr;
   L->device = -1;
 }
 
@@ -188,7 +196,8 @@ int radial_layout_upload(radial_layout *L) {
   if (forced_alloc_failure()) return fail(RADIAL_E_NOMEM, "allocation failure (forced by test hook)");
   const size_t nb1 = (size_t)L->nb + 1, nz = (size_t)L->nnz_tiles, nb = (size_t)L->nb;
   const size_t words =
-      2 * nb1 + 2 * nz + nb + L->band_rtab.size() + L->pair_ptr.size() + L->pair_idx.size();
+      2 * nb1 + 2 * nz + nb + L->band_rtab.size() + L->pair_ptr.size() + L->pair_idx.size() +
+      L->tri_ptr.size() + L->tri_idx.size();
   void *p = nullptr;
   if (hipMalloc(&p, words * sizeof(int32_t)) != hipSuccess || !p) {
     (void)hipGetLastError();
@@ -220,7 +229,9 @@ int radial_layout_upload(radial_layout *L) {
                {&L->col_order, &L->d_col_order},
                {&L->band_rtab, &L->d_band_rtab},
                {&L->pair_ptr, &L->d_pair_ptr},
-               {&L->pair_idx, &L->d_pair_idx}};
+               {&L->pair_idx, &L->d_pair_idx},
+               {&L->tri_ptr, &L->d_tri_ptr},
+               {&L->tri_idx, &L->d_tri_idx}};
   for (auto &pt : parts) {
     const size_t cnt = pt.src->size();
     if (cnt && hipMemcpy(b + off, pt.src->data(), cnt * sizeof(int32_t),
@@ -229,7 +240,7 @@ int radial_layout_upload(radial_layout *L) {
       (void)hipGetLastError();
       return fail(RADIAL_E_HIP, "hipMemcpy of the layout failed");
     }
-    *pt.dst = cnt ? b + off : nullptr;  // empty arrays (pair lists not built) stay null
+    *pt.dst = cnt ? b + off : nullptr;  // empty arrays (group lists not built) stay null
     off += cnt;
   }
   L->d_base = p;
@@ -286,6 +297,9 @@ int radial_attn_fwd(const radial_layout *L, int32_t B, int32_t H, int64_t N, int
   a.col_idx = L->d_col_idx;
   a.pair_ptr = L->d_pair_ptr;
   a.pair_idx = L->d_pair_idx;
+  a.tri_ptr = L->d_tri_ptr;
+  a.tri_idx = L->d_tri_idx;
+  a.max_group = forced_max_group();
   a.BH = B * H;
   a.N = static_cast<int32_t>(N);
   a.D = D;

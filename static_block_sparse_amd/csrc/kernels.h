@@ -13,6 +13,13 @@ constexpr int32_t kPairTile = (1 << 27) - 1;
 constexpr int32_t kPairInA = 1 << 27, kPairInB = 1 << 28;
 constexpr int32_t kPairPartA = 1 << 29, kPairPartB = 1 << 30;
 
+// Fields of an entry of the forward pass's triple lists (per triple of query
+// tiles 3t, 3t + 1, 3t + 2, the sorted union of their key tiles): the key
+// tile, membership bit kTriIn << k and partial-tile bit kTriPart << k for
+// row 3t + k of the triple.
+constexpr int32_t kTriTile = (1 << 25) - 1;
+constexpr int32_t kTriIn = 1 << 25, kTriPart = 1 << 28;
+
 // What the kernels need of the mask to apply it token by token inside the
 // tiles a token-exact layout marks partial (bit 31 of the tile indices).
 struct MaskGeom {
@@ -38,8 +45,12 @@ struct FwdArgs {
   void *o;
   float *lse;
   const int32_t *row_ptr, *col_idx;  // device CSR of the layout
-  // per pair of query tiles: the union of their key tiles (see layout.h)
+  // per pair / triple of query tiles: the union of their key tiles (see
+  // layout.h); null when not built
   const int32_t *pair_ptr, *pair_idx;
+  const int32_t *tri_ptr, *tri_idx;
+  // largest query-tile group the forward may use (3; lower only in tests)
+  int32_t max_group;
   int32_t BH, N, D, T, nb;
   float scale;
   MaskGeom mask;

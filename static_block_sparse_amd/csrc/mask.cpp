@@ -241,35 +241,48 @@ std::string build_layout(int64_t frames, int64_t s, int32_t T, uint32_t flags,
     }
   }
 
-  // forward pairs: the union of the key tiles of query tiles 2p and 2p + 1
-  L.pair_ptr.clear();
-  L.pair_idx.clear();
-  if (nb <= kPairTile) {
-    const int64_t np = (nb + 1) / 2;
-    L.pair_ptr.assign(np + 1, 0);
-    L.pair_idx.reserve(L.nnz_tiles);
-    for (int64_t pr = 0; pr < np; ++pr) {
-      const int64_t ua = 2 * pr, ub = 2 * pr + 1;
-      int32_t i = L.row_ptr[ua], ie = L.row_ptr[ua + 1];
-      int32_t j = ub < nb ? L.row_ptr[ub] : 0, je = ub < nb ? L.row_ptr[ub + 1] : 0;
-      while (i < ie || j < je) {
-        const int32_t a = i < ie ? L.col_idx[i] : INT32_MAX;
-        const int32_t b = j < je ? L.col_idx[j] : INT32_MAX;
-        const int32_t v = a < b ? a : b;
-        int32_t e = v;
-        if (a == v) {
-          e |= kPairInA | (L.full[i] ? 0 : kPairPartA);
-          ++i;
+  // forward groups: per G consecutive query tiles, the sorted union of their
+  // key tiles, each entry tagged with a membership bit and a partial bit per
+  // tile of the group (pairs: the kPair fields; triples: the kTri fields)
+  auto build_groups = [&](int G, int32_t tile_mask, const int32_t *in_bit,
+                          const int32_t *part_bit, std::vector<int32_t> &ptr,
+                          std::vector<int32_t> &idx) {
+    ptr.clear();
+    idx.clear();
+    if (nb > tile_mask) return;
+    const int64_t ng = (nb + G - 1) / G;
+    ptr.assign(ng + 1, 0);
+    idx.reserve(L.nnz_tiles);
+    for (int64_t gi = 0; gi < ng; ++gi) {
+      int32_t pos[3] = {0, 0, 0}, end[3] = {0, 0, 0};
+      for (int k = 0; k < G; ++k) {
+        const int64_t u = G * gi + k;
+        if (u < nb) {
+          pos[k] = L.row_ptr[u];
+          end[k] = L.row_ptr[u + 1];
         }
-        if (b == v) {
-          e |= kPairInB | (L.full[j] ? 0 : kPairPartB);
-          ++j;
-        }
-        L.pair_idx.push_back(e);
       }
-      L.pair_ptr[pr + 1] = static_cast<int32_t>(L.pair_idx.size());
+      for (;;) {
+        int32_t v = INT32_MAX;
+        for (int k = 0; k < G; ++k)
+          if (pos[k] < end[k] && L.col_idx[pos[k]] < v) v = L.col_idx[pos[k]];
+        if (v == INT32_MAX) break;
+        int32_t e = v;
+        for (int k = 0; k < G; ++k)
+          if (pos[k] < end[k] && L.col_idx[pos[k]] == v) {
+            e |= in_bit[k] | (L.full[pos[k]] ? 0 : part_bit[k]);
+            ++pos[k];
+          }
+        idx.push_back(e);
+      }
+      ptr[gi + 1] = static_cast<int32_t>(idx.size());
     }
-  }
+  };
+  const int32_t pair_in[3] = {kPairInA, kPairInB, 0}, pair_part[3] = {kPairPartA, kPairPartB, 0};
+  build_groups(2, kPairTile, pair_in, pair_part, L.pair_ptr, L.pair_idx);
+  const int32_t tri_in[3] = {kTriIn, kTriIn << 1, kTriIn << 2};
+  const int32_t tri_part[3] = {kTriPart, kTriPart << 1, kTriPart << 2};
+  build_groups(3, kTriTile, tri_in, tri_part, L.tri_ptr, L.tri_idx);
 
   // transpose to CSC (query tiles ascending within each key tile)
   L.col_ptr.assign(nb + 1, 0);

@@ -58,33 +58,46 @@ void check_mask(const radial::MaskGeom &m) {
   check(m.s_shift >= 31 && m.s_shift <= 62, "division shift");
 }
 
-// pair lists: for query tiles 2p and 2p + 1, the sorted union of their CSR
-// rows, each entry marked with its membership bits
-void check_pairs(const int32_t *row_ptr, const int32_t *col_idx, const int32_t *pair_ptr,
-                 const int32_t *pair_idx, int32_t nb) {
-  check(pair_ptr != nullptr && pair_idx != nullptr, "pair lists uploaded");
-  if (!pair_ptr || !pair_idx) return;
-  const int32_t np = (nb + 1) / 2;
-  check(pair_ptr[0] == 0, "pair lists start");
-  for (int32_t p = 0; p < np; ++p) {
-    int32_t i = row_ptr[2 * p], ie = row_ptr[2 * p + 1];
-    int32_t j = 2 * p + 1 < nb ? row_ptr[2 * p + 1] : 0;
-    int32_t je = 2 * p + 1 < nb ? row_ptr[2 * p + 2] : 0;
+// group lists: for query tiles G g .. G g + G - 1, the sorted union of their
+// CSR rows, each entry marked with a membership bit per row (in << k) and, in
+// token-exact uploads, a partial bit per member row (part << k) equal to the
+// partial mark (bit 31) of that row's CSR entry
+void check_groups(int G, const int32_t *row_ptr, const int32_t *col_idx, const int32_t *gptr,
+                  const int32_t *gidx, int32_t nb, int32_t tile_mask, int32_t in, int32_t part,
+                  bool exact) {
+  check(gptr != nullptr && gidx != nullptr, "group lists uploaded");
+  if (!gptr || !gidx) return;
+  const int32_t ng = (nb + G - 1) / G;
+  check(gptr[0] == 0, "group lists start");
+  for (int32_t g = 0; g < ng; ++g) {
+    int32_t pos[3] = {0, 0, 0}, end[3] = {0, 0, 0};
+    for (int k = 0; k < G; ++k)
+      if (G * g + k < nb) {
+        pos[k] = row_ptr[G * g + k];
+        end[k] = row_ptr[G * g + k + 1];
+      }
     int32_t prev = -1;
-    for (int32_t t = pair_ptr[p]; t < pair_ptr[p + 1]; ++t) {
-      const int32_t e = pair_idx[t], v = e & radial::kPairTile;
-      check(v > prev && v < nb, "pair list sorted, in range");
+    for (int32_t t = gptr[g]; t < gptr[g + 1]; ++t) {
+      const int32_t e = gidx[t], v = e & tile_mask;
+      check(v > prev && v < nb, "group list sorted, in range");
       prev = v;
-      const bool in_a = i < ie && (col_idx[i] & 0x7fffffff) == v;
-      const bool in_b = j < je && (col_idx[j] & 0x7fffffff) == v;
-      check(in_a || in_b, "pair entry comes from a row");
-      check(((e & radial::kPairInA) != 0) == in_a && ((e & radial::kPairInB) != 0) == in_b,
-            "membership bits");
-      if (in_a) ++i;
-      if (in_b) ++j;
+      bool any = false;
+      for (int k = 0; k < G; ++k) {
+        const bool mem = pos[k] < end[k] && (col_idx[pos[k]] & 0x7fffffff) == v;
+        check(((e & (in << k)) != 0) == mem, "membership bits");
+        if (mem && exact) check(((e & (part << k)) != 0) == (col_idx[pos[k]] < 0), "partial bits");
+        if (mem) ++pos[k];
+        any = any || mem;
+      }
+      check(any, "group entry comes from a row");
     }
-    check(i == ie && j == je, "pair list covers both rows");
+    for (int k = 0; k < G; ++k) check(pos[k] == end[k], "group list covers every row");
   }
+}
+void check_pairs(const int32_t *row_ptr, const int32_t *col_idx, const int32_t *pair_ptr,
+                 const int32_t *pair_idx, int32_t nb, bool exact) {
+  check_groups(2, row_ptr, col_idx, pair_ptr, pair_idx, nb, radial::kPairTile, radial::kPairInA,
+               radial::kPairPartA, exact);
 }
 
 }  // namespace
@@ -125,7 +138,10 @@ hipError_t launch_fwd(const FwdArgs &a, hipStream_t) {
   write_range(a.o, x);
   write_range(a.lse, r);
   check_lists(a.row_ptr, a.col_idx, a.nb, "forward CSR");
-  check_pairs(a.row_ptr, a.col_idx, a.pair_ptr, a.pair_idx, a.nb);
+  check_pairs(a.row_ptr, a.col_idx, a.pair_ptr, a.pair_idx, a.nb, a.mask.exact);
+  check_groups(3, a.row_ptr, a.col_idx, a.tri_ptr, a.tri_idx, a.nb, radial::kTriTile,
+               radial::kTriIn, radial::kTriPart, a.mask.exact);
+  check(a.max_group >= 1 && a.max_group <= 3, "forward group cap");
   check_mask(a.mask);
   return hipSuccess;
 }
@@ -141,7 +157,7 @@ hipError_t launch_bwd(const BwdArgs &a, hipStream_t) {
   check(a.nlse2 >= a.ndelta + size_t(a.BH) * a.N, "workspace arrays overlap");
   check_lists(a.row_ptr, a.col_idx, a.nb, "backward CSR");
   check_lists(a.col_ptr, a.row_idx, a.nb, "backward CSC");
-  check_pairs(a.row_ptr, a.col_idx, a.pair_ptr, a.pair_idx, a.nb);
+  check_pairs(a.row_ptr, a.col_idx, a.pair_ptr, a.pair_idx, a.nb, a.mask.exact);
   // col_order: a permutation of the key tiles
   unsigned char *seen = static_cast<unsigned char *>(std::calloc(a.nb, 1));
   for (int32_t i = 0; i < a.nb; ++i) {

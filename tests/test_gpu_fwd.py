@@ -109,6 +109,35 @@ def test_two_frames_equal_dense_layout_bitwise():
     assert torch.equal(a, b) and torch.equal(la, lb)
 
 
+@pytest.mark.parametrize("f,s,T,D,exact", [
+    (8, 256, 64, 64, False),     # the tiny workload's shape
+    (7, 100, 64, 64, True),      # ragged, 64-tiles spanning frames, token-exact
+    (5, 300, 128, 128, False),   # ragged last tile, 12 tiles (4 triples)
+    (13, 100, 128, 128, True),   # 11 tiles: a last triple of two, token-exact
+    (9, 100, 128, 64, False),    # head dim 64 on 128-wide tiles, odd tile count
+])
+def test_query_tile_groups_agree_bitwise(f, s, T, D, exact, monkeypatch):
+    # single tiles, pairs and triples: each wave walks its own kept tiles in
+    # the same order whatever the group, so the results are the same bits
+    q, k, v = (t.cuda() for t in workloads.make_inputs(1, 2, f * s, D, 81))
+    L = sba.Layout(f, s, T, token_exact=exact)
+    out = {}
+    for cap in ("1", "2", "3"):
+        if cap == "3":
+            monkeypatch.delenv("RADIAL_TEST_FWD_GROUP", raising=False)
+        else:
+            monkeypatch.setenv("RADIAL_TEST_FWD_GROUP", cap)
+        out[cap] = sba.attn_fwd(q, k, v, L)
+    monkeypatch.delenv("RADIAL_TEST_FWD_GROUP", raising=False)
+    for cap in ("1", "2"):
+        assert torch.equal(out[cap][0], out["3"][0]) and torch.equal(out[cap][1], out["3"][1]), cap
+    kept = om.kept_tiles(f, s, T, True)
+    if not exact:
+        ro, rl = oa.fwd(f64(q[0, 0]), f64(k[0, 0]), f64(v[0, 0]), kept, T, 1.0 / np.sqrt(D))
+        check_close(f64(out["3"][0][0, 0]), ro, "O")
+        check_lse(f64(out["3"][1][0, 0]), rl, "LSE")
+
+
 def test_deterministic_and_stream_aware():
     f, s, T, D = 6, 300, 128, 128
     q, k, v = (t.cuda() for t in workloads.make_inputs(2, 3, f * s, D, 71))
