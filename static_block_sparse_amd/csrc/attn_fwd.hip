@@ -1,6 +1,7 @@
 // Radial block-sparse attention forward on gfx950.
 //
-// One workgroup computes one query tile u (T rows) of one (batch, head):
+// A workgroup computes G query tiles u (T rows each) of one (batch, head);
+// for every u (with its own waves):
 //   for each kept key tile v of row u (CSR, ascending), in chunks of KC keys:
 //     S^T = K_c Q_u^T                (bf16 MFMA, fp32 accumulate)
 //     online softmax over keys       (running max and sum per query, fp32)
@@ -12,7 +13,7 @@
 // kept tiles of the radial mask (Step 5; paper §4.2), with keys >= N masked.
 //
 // Layout of the work:
-//  * wave w owns queries [32w, 32w + 32) of the tile; its Q rows stay in
+//  * wave w owns queries [32w, 32w + 32) of its tile; its Q rows stay in
 //    registers as the B operand of S^T = K Q^T.  Computing S transposed puts
 //    one query per lane column: a row's max and sum need one exchange
 //    between lanes l and l ^ 32 (v_permlane32_swap), and P feeds P V as the
@@ -124,8 +125,8 @@ radial_fwd_kernel(const bf16 *__restrict__ Q, const bf16 *__restrict__ K,
 
   // chunk list: every KC-key chunk of every listed key tile, minus the
   // chunks of the last key tile that lie entirely at or beyond N.  A list
-  // entry is a key tile (CSR: bit 31 marks a partial tile; pair lists:
-  // membership and partial bits per tile of the pair, see kernels.h).
+  // entry is a key tile (CSR: bit 31 marks a partial tile; pair and triple
+  // lists: membership and partial bits per tile of the group, see kernels.h).
   const int32_t *lptr = G > 1 ? grp_ptr : row_ptr;
   const int32_t *lidx = G > 1 ? grp_idx : col_idx;
   constexpr int32_t TMASK = GB::kTile;
