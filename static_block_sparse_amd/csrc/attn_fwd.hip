@@ -225,7 +225,9 @@ radial_fwd_kernel(const bf16 *__restrict__ Q, const bf16 *__restrict__ K,
 
     if (member) {
       // S^T for the wave's 32 queries against the chunk's KC keys, the K
-      // fragments read four products ahead (products in the order kk, kb)
+      // fragments read four products ahead (products in the order kk, kb);
+      // two in token-exact mode, whose predicate needs registers of its own
+      // (with four, triples spill inside the chunk loop there)
       f32x16 s[C::NKB];
       bf16x8 kf[C::NKB][C::NKK];
 #pragma unroll
@@ -239,7 +241,7 @@ radial_fwd_kernel(const bf16 *__restrict__ Q, const bf16 *__restrict__ K,
       for (int kk = 0; kk < C::NKK; ++kk)
 #pragma unroll
         for (int kb = 0; kb < C::NKB; ++kb) s[kb] = mfma32(kf[kb][kk], qf[kk], s[kb]);
-      read_ahead_order<1, 4, C::NKK * C::NKB, 1>();
+      read_ahead_order<1, EXACT ? 2 : 4, C::NKK * C::NKB, 1>();
       if (key0 + C::KC > N) {  // the tail chunk: keys at or past N get -inf
         // register r of block kb holds key key0 + kb*32 + 8*(r/4) + 4g + r%4
         const int lim = N - key0 - 4 * g;
