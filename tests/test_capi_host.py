@@ -44,6 +44,19 @@ def test_library_exports_every_declared_symbol():
     assert set(names) <= exported
 
 
+def test_binding_argument_counts_match_header():
+    # every prototype's parameter count equals the ctypes argtypes the
+    # binding installs (a missing or extra argument shifts every later one)
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    protos = re.findall(r"\b(radial_[a-z_0-9]+)\s*\(([^;{]*?)\)\s*;", text, flags=re.S)
+    lib = sba.lib()
+    assert len(protos) >= 12
+    for name, params in protos:
+        params = params.strip()
+        n = 0 if params in ("", "void") else params.count(",") + 1
+        assert len(getattr(lib, name).argtypes) == n, name
+
+
 SMALL = [(4, 9, 4), (8, 256, 64), (5, 7, 3), (33, 3, 16), (12, 1, 4), (6, 100, 64),
          (3, 50, 128), (40, 2, 7), (20, 33, 32), (66, 256, 128), (17, 100, 64), (1, 5, 2),
          (2, 300, 128), (9, 130, 128)]
