@@ -29,14 +29,17 @@
 //  * the running max is only moved when a chunk's max exceeds it by more
 //    than 8 (log2 units); probabilities then stay below 2^8, exact in the
 //    final O / l and LSE, and the O rescale is skipped on most chunks.
-//  * query-tile groups: a workgroup of G T / 32 waves takes G adjacent
-//    query tiles (G = 3, three waves per SIMD; pairs or single tiles only
-//    when the mask compiler built no triple lists) and walks the sorted
-//    union of their key tiles.  Every staged chunk then serves G tiles'
-//    waves, which divides the global -> LDS copies per product by about G;
-//    at the power cap the copies' energy is a large share of the budget.
-//    A wave skips the chunks of key tiles its own tile does not keep (6% of
-//    a pair's walk, 12% of a triple's, for the radial mask at 720p).
+//  * query-tile groups: a workgroup of G T / 32 waves takes G query tiles
+//    (G = 3, three waves per SIMD; pairs or single tiles only when the mask
+//    compiler built no triple lists) and walks the sorted union of their key
+//    tiles.  Every staged chunk then serves G tiles' waves, which divides
+//    the global -> LDS copies per product by about G; at the power cap the
+//    copies' energy is a large share of the budget.  A wave skips the chunks
+//    of key tiles its own tile does not keep.  Pairs are adjacent tiles
+//    (6% of a pair's walk skipped at 720p); the mask compiler picks triples
+//    that share key tiles, often the tiles at one place in neighbouring
+//    frames (10% of a triple's walk skipped at 720p, 10% at 129 frames,
+//    against 12% and 23% for adjacent tiles).
 //  * token-exact layouts (EXACT): in the chunks of tiles marked partial,
 //    each lane masks the keys outside its query's allowed runs (one per key
 //    frame the chunk touches, however many) before the max.
@@ -90,7 +93,8 @@ radial_fwd_kernel(const bf16 *__restrict__ Q, const bf16 *__restrict__ K,
                   const bf16 *__restrict__ V, bf16 *__restrict__ O, float *__restrict__ LSE,
                   const int32_t *__restrict__ row_ptr, const int32_t *__restrict__ col_idx,
                   const int32_t *__restrict__ grp_ptr, const int32_t *__restrict__ grp_idx,
-                  int32_t N, int32_t nb, int32_t n_work, float scale_log2, MaskGeom mg) {
+                  const int32_t *__restrict__ grp_tiles, int32_t n_grp, int32_t N, int32_t nb,
+                  int32_t n_work, float scale_log2, MaskGeom mg) {
   using C = FwdCfg<D, T, G>;
   using GB = GroupBits<G>;
   constexpr float kSlack = 8.f;  // lazy-rescale threshold (log2 units)
@@ -99,15 +103,18 @@ radial_fwd_kernel(const bf16 *__restrict__ Q, const bf16 *__restrict__ K,
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c32 = lane & 31, g = lane >> 5;
-  // work item: G query tiles G p + k (waves [k NWR, (k + 1) NWR)) over the
-  // union of their key tiles, so every staged K/V chunk serves G times the
-  // queries
-  const int nwork_head = (nb + G - 1) / G;
+  // work item: G query tiles (waves [k NWR, (k + 1) NWR) take tile k) over
+  // the union of their key tiles, so every staged K/V chunk serves G times
+  // the queries; pairs are tiles 2 p + k, triples the listed ones
   const int work = xcd_remap(blockIdx.x, n_work, RADIAL_FWD_XCD_BLOCK);
-  const int bh = work / nwork_head;
-  const int wi = work - bh * nwork_head;
+  const int bh = work / n_grp;
+  const int wi = work - bh * n_grp;
   const int sub = G > 1 ? wave / C::NWR : 0;  // which tile of the group
-  const int u = G * wi + sub;
+  int u = G * wi + sub;
+  if constexpr (G == 3) {
+    u = grp_tiles[3 * wi + sub];
+    if (u < 0) u = nb;  // no tile: the waves only help with the copies
+  }
   const int64_t base = (int64_t)bh * N * D;
   const bf16 *Kb = K + base;
   const bf16 *Vb = V + base;
@@ -344,12 +351,14 @@ radial_fwd_kernel(const bf16 *__restrict__ Q, const bf16 *__restrict__ K,
 
 template <int D, int T, bool EXACT, int G>
 hipError_t launch_fwd_t(const FwdArgs &a, hipStream_t stream) {
-  const int64_t works = (int64_t)a.BH * ((a.nb + G - 1) / G);
+  const int32_t n_grp = G == 3 ? a.n_tri : (a.nb + G - 1) / G;
+  const int64_t works = (int64_t)a.BH * n_grp;
   hipLaunchKernelGGL((radial_fwd_kernel<D, T, EXACT, G>), dim3((unsigned)works),
                      dim3(FwdCfg<D, T, G>::NT), 0, stream, (const bf16 *)a.q,
                      (const bf16 *)a.k, (const bf16 *)a.v, (bf16 *)a.o, a.lse, a.row_ptr,
                      a.col_idx, G == 3 ? a.tri_ptr : a.pair_ptr,
-                     G == 3 ? a.tri_idx : a.pair_idx, a.N, a.nb, (int32_t)works,
+                     G == 3 ? a.tri_idx : a.pair_idx, a.tri_tiles, n_grp, a.N, a.nb,
+                     (int32_t)works,
                      a.scale * kLog2e, a.mask);
   return hipGetLastError();
 }
@@ -358,7 +367,7 @@ hipError_t launch_fwd_t(const FwdArgs &a, hipStream_t stream) {
 // has the group lists and max_group allows.
 template <int D, int T, bool EXACT>
 hipError_t launch_fwd_g(const FwdArgs &a, hipStream_t stream) {
-  if (a.max_group >= 3 && a.tri_ptr) return launch_fwd_t<D, T, EXACT, 3>(a, stream);
+  if (a.max_group >= 3 && a.tri_ptr && a.tri_tiles) return launch_fwd_t<D, T, EXACT, 3>(a, stream);
   if (a.max_group >= 2 && a.pair_ptr) return launch_fwd_t<D, T, EXACT, 2>(a, stream);
   return launch_fwd_t<D, T, EXACT, 1>(a, stream);
 }

@@ -51,6 +51,7 @@ void free_device(radial_layout *L) {
   L->d_base = nullptr;
   L->d_row_ptr = L->d_col_idx = L->d_col_ptr = L->d_row_idx = L->d_col_order = nullptr;
   L->d_band_rtab = L->d_pair_ptr = L->d_pair_idx = L->d_tri_ptr = L->d_tri_idx = nullptr;
+  L->d_tri_tiles = nullptr;
   L->device = -1;
 }
 
@@ -197,7 +198,7 @@ int radial_layout_upload(radial_layout *L) {
   const size_t nb1 = (size_t)L->nb + 1, nz = (size_t)L->nnz_tiles, nb = (size_t)L->nb;
   const size_t words =
       2 * nb1 + 2 * nz + nb + L->band_rtab.size() + L->pair_ptr.size() + L->pair_idx.size() +
-      L->tri_ptr.size() + L->tri_idx.size();
+      L->tri_ptr.size() + L->tri_idx.size() + L->tri_tiles.size();
   void *p = nullptr;
   if (hipMalloc(&p, words * sizeof(int32_t)) != hipSuccess || !p) {
     (void)hipGetLastError();
@@ -231,7 +232,8 @@ int radial_layout_upload(radial_layout *L) {
                {&L->pair_ptr, &L->d_pair_ptr},
                {&L->pair_idx, &L->d_pair_idx},
                {&L->tri_ptr, &L->d_tri_ptr},
-               {&L->tri_idx, &L->d_tri_idx}};
+               {&L->tri_idx, &L->d_tri_idx},
+               {&L->tri_tiles, &L->d_tri_tiles}};
   for (auto &pt : parts) {
     const size_t cnt = pt.src->size();
     if (cnt && hipMemcpy(b + off, pt.src->data(), cnt * sizeof(int32_t),
@@ -299,6 +301,8 @@ int radial_attn_fwd(const radial_layout *L, int32_t B, int32_t H, int64_t N, int
   a.pair_idx = L->d_pair_idx;
   a.tri_ptr = L->d_tri_ptr;
   a.tri_idx = L->d_tri_idx;
+  a.tri_tiles = L->d_tri_tiles;
+  a.n_tri = static_cast<int32_t>(L->tri_tiles.size() / 3);
   a.max_group = forced_max_group();
   a.BH = B * H;
   a.N = static_cast<int32_t>(N);

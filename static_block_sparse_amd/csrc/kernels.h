@@ -49,6 +49,8 @@ struct FwdArgs {
   // layout.h); null when not built
   const int32_t *pair_ptr, *pair_idx;
   const int32_t *tri_ptr, *tri_idx;
+  const int32_t *tri_tiles;  // the query tiles of each triple (3 each, -1: none)
+  int32_t n_tri;             // triples per (batch, head)
   // largest query-tile group the forward may use (3; lower only in tests)
   int32_t max_group;
   int32_t BH, N, D, T, nb;

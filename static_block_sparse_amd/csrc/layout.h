@@ -33,16 +33,18 @@ struct radial_layout {
   // 2p / 2p + 1) | kPairPartA | kPairPartB (partial in that row).  Built when
   // the tile index fits below 2^27 (every supported tile size).
   std::vector<int32_t> pair_ptr, pair_idx;
-  // the same per triple of query tiles (3t, 3t + 1, 3t + 2): entry = key tile
-  // | kTriIn << k (member of row 3t + k) | kTriPart << k (partial in that
-  // row).  Built when the tile index fits below 2^25.
-  std::vector<int32_t> tri_ptr, tri_idx;
+  // the same per triple of query tiles tri_tiles[3t + k], k < 3 (-1: no
+  // tile), chosen to share key tiles (see group_triples): entry = key tile
+  // | kTriIn << k (member of row tri_tiles[3t + k]) | kTriPart << k (partial
+  // in that row).  Built when the tile index fits below 2^25.
+  std::vector<int32_t> tri_tiles, tri_ptr, tri_idx;
   // full[t] = 1 when every valid token pair of CSR tile t is allowed (no
   // masking needed under token-exact semantics), else 0; full_csc in CSC order
   std::vector<uint8_t> full, full_csc;
 
   // device copy (one allocation): row_ptr | col_idx | col_ptr | row_idx |
-  // col_order | band_rtab | pair_ptr | pair_idx | tri_ptr | tri_idx
+  // col_order | band_rtab | pair_ptr | pair_idx | tri_ptr | tri_idx |
+  // tri_tiles
   int device = -1;
   void *d_base = nullptr;
   const int32_t *d_row_ptr = nullptr;
@@ -55,6 +57,7 @@ struct radial_layout {
   const int32_t *d_pair_idx = nullptr;
   const int32_t *d_tri_ptr = nullptr;
   const int32_t *d_tri_idx = nullptr;
+  const int32_t *d_tri_tiles = nullptr;
 };
 
 namespace radial {

@@ -50,6 +50,55 @@
 #include "radial.h"
 
 namespace radial {
+
+// Triples of query tiles for the forward, three tiles per triple (-1: none).
+// A greedy pass in tile order puts each tile not yet grouped with the two
+// ungrouped tiles among the next W that leave its group the fewest key tiles
+// outside their own rows (ties: the nearest).  W spans two frames of tiles:
+// tiles at the same place in neighbouring frames select nearly the same key
+// tiles in the narrow far bands, where adjacent tiles of one frame do not.
+// Consecutive triples when the layout is too large for the search.
+static std::vector<int32_t> group_triples(const radial_layout &L) {
+  const int64_t nb = L.nb, T = L.block, s = L.tokens_per_frame;
+  const int64_t W = std::min<int64_t>(256, 2 * ((s + T - 1) / T) + 2);
+  const int64_t words = (nb + 63) / 64;
+  std::vector<int32_t> out;
+  if (nb * words > (int64_t(1) << 23) || nb * W * words > (int64_t(1) << 30)) {
+    for (int64_t u = 0; u < nb; u += 3)
+      for (int64_t k = 0; k < 3; ++k) out.push_back(u + k < nb ? int32_t(u + k) : -1);
+    return out;
+  }
+  std::vector<uint64_t> rows(nb * words, 0), un(words);
+  for (int64_t u = 0; u < nb; ++u)
+    for (int32_t t = L.row_ptr[u]; t < L.row_ptr[u + 1]; ++t)
+      rows[u * words + L.col_idx[t] / 64] |= uint64_t(1) << (L.col_idx[t] % 64);
+  std::vector<uint8_t> used(nb, 0);
+  for (int64_t u = 0; u < nb; ++u) {
+    if (used[u]) continue;
+    used[u] = 1;
+    std::copy(rows.begin() + u * words, rows.begin() + (u + 1) * words, un.begin());
+    int32_t g[3] = {int32_t(u), -1, -1};
+    for (int k = 1; k < 3; ++k) {
+      int64_t best = -1, best_cost = INT64_MAX;
+      for (int64_t v = u + 1; v < nb && v <= u + W; ++v) {
+        if (used[v]) continue;
+        const uint64_t *rv = &rows[v * words];
+        int64_t cost = 0;  // key tiles of the group outside row v
+        for (int64_t w = 0; w < words; ++w) cost += __builtin_popcountll(un[w] & ~rv[w]);
+        if (cost < best_cost) {
+          best_cost = cost;
+          best = v;
+        }
+      }
+      if (best < 0) break;
+      used[best] = 1;
+      g[k] = int32_t(best);
+      for (int64_t w = 0; w < words; ++w) un[w] |= rows[best * words + w];
+    }
+    out.insert(out.end(), g, g + 3);
+  }
+  return out;
+}
 namespace {
 
 inline int bit_length(uint64_t x) { return x == 0 ? 0 : 64 - __builtin_clzll(x); }
@@ -241,23 +290,24 @@ std::string build_layout(int64_t frames, int64_t s, int32_t T, uint32_t flags,
     }
   }
 
-  // forward groups: per G consecutive query tiles, the sorted union of their
+  // forward groups: per G query tiles (G consecutive ones, or those that
+  // `members` lists, G per group, -1 for none), the sorted union of their
   // key tiles, each entry tagged with a membership bit and a partial bit per
   // tile of the group (pairs: the kPair fields; triples: the kTri fields)
   auto build_groups = [&](int G, int32_t tile_mask, const int32_t *in_bit,
-                          const int32_t *part_bit, std::vector<int32_t> &ptr,
-                          std::vector<int32_t> &idx) {
+                          const int32_t *part_bit, const std::vector<int32_t> *members,
+                          std::vector<int32_t> &ptr, std::vector<int32_t> &idx) {
     ptr.clear();
     idx.clear();
     if (nb > tile_mask) return;
-    const int64_t ng = (nb + G - 1) / G;
+    const int64_t ng = members ? int64_t(members->size()) / G : (nb + G - 1) / G;
     ptr.assign(ng + 1, 0);
     idx.reserve(L.nnz_tiles);
     for (int64_t gi = 0; gi < ng; ++gi) {
       int32_t pos[3] = {0, 0, 0}, end[3] = {0, 0, 0};
       for (int k = 0; k < G; ++k) {
-        const int64_t u = G * gi + k;
-        if (u < nb) {
+        const int64_t u = members ? (*members)[G * gi + k] : G * gi + k;
+        if (u >= 0 && u < nb) {
           pos[k] = L.row_ptr[u];
           end[k] = L.row_ptr[u + 1];
         }
@@ -279,10 +329,12 @@ std::string build_layout(int64_t frames, int64_t s, int32_t T, uint32_t flags,
     }
   };
   const int32_t pair_in[3] = {kPairInA, kPairInB, 0}, pair_part[3] = {kPairPartA, kPairPartB, 0};
-  build_groups(2, kPairTile, pair_in, pair_part, L.pair_ptr, L.pair_idx);
+  build_groups(2, kPairTile, pair_in, pair_part, nullptr, L.pair_ptr, L.pair_idx);
   const int32_t tri_in[3] = {kTriIn, kTriIn << 1, kTriIn << 2};
   const int32_t tri_part[3] = {kTriPart, kTriPart << 1, kTriPart << 2};
-  build_groups(3, kTriTile, tri_in, tri_part, L.tri_ptr, L.tri_idx);
+  L.tri_tiles = group_triples(L);
+  build_groups(3, kTriTile, tri_in, tri_part, &L.tri_tiles, L.tri_ptr, L.tri_idx);
+  if (L.tri_ptr.empty()) L.tri_tiles.clear();
 
   // transpose to CSC (query tiles ascending within each key tile)
   L.col_ptr.assign(nb + 1, 0);

@@ -12,6 +12,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <vector>
 
 #include "kernels.h"
 
@@ -62,20 +63,33 @@ void check_mask(const radial::MaskGeom &m) {
 // CSR rows, each entry marked with a membership bit per row (in << k) and, in
 // token-exact uploads, a partial bit per member row (part << k) equal to the
 // partial mark (bit 31) of that row's CSR entry
+// tiles: the query tiles of each group (G per group, -1 for none; every
+// tile exactly once), or null for groups of consecutive tiles
 void check_groups(int G, const int32_t *row_ptr, const int32_t *col_idx, const int32_t *gptr,
-                  const int32_t *gidx, int32_t nb, int32_t tile_mask, int32_t in, int32_t part,
-                  bool exact) {
+                  const int32_t *gidx, const int32_t *tiles, int32_t ng, int32_t nb,
+                  int32_t tile_mask, int32_t in, int32_t part, bool exact) {
   check(gptr != nullptr && gidx != nullptr, "group lists uploaded");
   if (!gptr || !gidx) return;
-  const int32_t ng = (nb + G - 1) / G;
+  if (!tiles) check(ng == (nb + G - 1) / G, "group count");
+  if (tiles) {
+    read_range(tiles, size_t(ng) * G * 4);
+    std::vector<int> seen(nb, 0);
+    for (int32_t i = 0; i < ng * G; ++i) {
+      check(tiles[i] >= -1 && tiles[i] < nb, "group tile in range");
+      if (tiles[i] >= 0) ++seen[tiles[i]];
+    }
+    for (int32_t u = 0; u < nb; ++u) check(seen[u] == 1, "every query tile in one group");
+  }
   check(gptr[0] == 0, "group lists start");
   for (int32_t g = 0; g < ng; ++g) {
     int32_t pos[3] = {0, 0, 0}, end[3] = {0, 0, 0};
-    for (int k = 0; k < G; ++k)
-      if (G * g + k < nb) {
-        pos[k] = row_ptr[G * g + k];
-        end[k] = row_ptr[G * g + k + 1];
+    for (int k = 0; k < G; ++k) {
+      const int32_t u = tiles ? tiles[G * g + k] : G * g + k;
+      if (u >= 0 && u < nb) {
+        pos[k] = row_ptr[u];
+        end[k] = row_ptr[u + 1];
       }
+    }
     int32_t prev = -1;
     for (int32_t t = gptr[g]; t < gptr[g + 1]; ++t) {
       const int32_t e = gidx[t], v = e & tile_mask;
@@ -96,8 +110,8 @@ void check_groups(int G, const int32_t *row_ptr, const int32_t *col_idx, const i
 }
 void check_pairs(const int32_t *row_ptr, const int32_t *col_idx, const int32_t *pair_ptr,
                  const int32_t *pair_idx, int32_t nb, bool exact) {
-  check_groups(2, row_ptr, col_idx, pair_ptr, pair_idx, nb, radial::kPairTile, radial::kPairInA,
-               radial::kPairPartA, exact);
+  check_groups(2, row_ptr, col_idx, pair_ptr, pair_idx, nullptr, (nb + 1) / 2, nb,
+               radial::kPairTile, radial::kPairInA, radial::kPairPartA, exact);
 }
 
 }  // namespace
@@ -139,8 +153,10 @@ hipError_t launch_fwd(const FwdArgs &a, hipStream_t) {
   write_range(a.lse, r);
   check_lists(a.row_ptr, a.col_idx, a.nb, "forward CSR");
   check_pairs(a.row_ptr, a.col_idx, a.pair_ptr, a.pair_idx, a.nb, a.mask.exact);
-  check_groups(3, a.row_ptr, a.col_idx, a.tri_ptr, a.tri_idx, a.nb, radial::kTriTile,
-               radial::kTriIn, radial::kTriPart, a.mask.exact);
+  check(a.tri_tiles != nullptr && a.n_tri >= (a.nb + 2) / 3 && a.n_tri <= a.nb, "triples");
+  if (a.tri_tiles)
+    check_groups(3, a.row_ptr, a.col_idx, a.tri_ptr, a.tri_idx, a.tri_tiles, a.n_tri, a.nb,
+                 radial::kTriTile, radial::kTriIn, radial::kTriPart, a.mask.exact);
   check(a.max_group >= 1 && a.max_group <= 3, "forward group cap");
   check_mask(a.mask);
   return hipSuccess;
