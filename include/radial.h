@@ -204,6 +204,9 @@ void radial_layout_destroy(radial_layout *L);
  *             masked logits of each query row (used by the backward pass).
  * N must equal the layout's n; (D, block_size) must be (64, 64),
  * (64, 128) or (128, 128); B, H >= 1; scale finite and > 0 (usually 1/sqrt(D)).
+ * One (batch, head) slice must hold fewer than 2^31 bytes (N * D * 2 < 2^31,
+ * i.e. N < 8,388,608 at D = 128): larger N returns RADIAL_E_UNSUPPORTED
+ * (checked before N is compared with the layout).
  * Products run on bf16 MFMA with fp32 accumulation and an fp32 online
  * softmax; the probabilities are rounded to bf16 before the P V product.
  */
@@ -220,7 +223,7 @@ size_t radial_attn_bwd_workspace_bytes(const radial_layout *L, int32_t B, int32_
  * radial_attn_bwd -- gradients of the forward above for an upstream
  * gradient dout = dL/dO: dq, dk, dv (bf16 [B, H, N, D], fully overwritten).
  * o and lse must be the forward's outputs for the same q, k, v, scale and
- * layout.  The probabilities are recomputed from lse; Delta = rowsum(dO*O)
+ * layout.  Shapes, limits and errors as radial_attn_fwd.  The probabilities are recomputed from lse; Delta = rowsum(dO*O)
  * and the exponent's row term are formed first in `workspace` (caller-owned
  * device memory of at least radial_attn_bwd_workspace_bytes bytes, 16-byte
  * aligned).  Deterministic:
@@ -230,6 +233,13 @@ int radial_attn_bwd(const radial_layout *L, int32_t B, int32_t H, int64_t N, int
                     float scale, const void *q, const void *k, const void *v, const void *o,
                     const float *lse, const void *dout, void *dq, void *dk, void *dv,
                     void *workspace, size_t workspace_bytes, void *hip_stream);
+
+/* Test hook: caps the query-tile grouping of every later radial_attn_fwd
+   call in the process at max_group tiles per workgroup (1 single tiles, 2
+   pairs, 3 triples, the default); the three forms give identical bits, and
+   tests compare them.  Returns the previous cap, or RADIAL_E_INVALID for a
+   value outside 1..3.  Not for concurrent use with forward calls. */
+int radial_test_set_fwd_group(int32_t max_group);
 
 /* Static text for a status code. */
 const char *radial_status_string(int status);

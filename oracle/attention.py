@@ -132,3 +132,44 @@ def bwd_dq_tile(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray,
     dp = do[rows] @ v[cols].T
     delta = (p * dp).sum(axis=1, keepdims=True)
     return scale * ((p * (dp - delta)) @ k[cols])
+
+
+def row_stats(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray,
+              kept: np.ndarray, T: int, scale: float, u: int) -> tuple[np.ndarray, np.ndarray]:
+    """LSE and Delta for the valid rows of query tile u: the log-sum-exp of
+    each row's logits over all of its kept keys, and Delta = <dO, O> with
+    O = P V over the same keys (the row terms of the textbook gradient)."""
+    o, lse = fwd_tile(q, k, v, kept, T, scale, u)
+    n = q.shape[0]
+    rows = slice(u * T, min(n, (u + 1) * T))
+    return lse, (do[rows] * o).sum(axis=1)
+
+
+def bwd_dkdv_tile(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray,
+                  kept: np.ndarray, T: int, scale: float, vt: int, stats=None):
+    """dK and dV for the valid key rows of key tile vt only.
+
+    The keys of tile vt receive gradient from every query row of every query
+    tile u whose row keeps vt (the tile map's column vt).  For each such row
+    the softmax runs over all of the row's own kept keys (its LSE), and the
+    textbook formulas restricted to the keys of vt give
+    dV_vt = sum_q P[q, vt]^T dO[q] and dK_vt = scale sum_q dS[q, vt]^T Q[q],
+    with dS = P (dP - Delta), dP = dO V_vt^T and Delta = <dO, O> of the row.
+    ``stats``: optional mapping u -> (LSE, Delta) of query tile u, as
+    ``row_stats`` returns (computed here when absent).
+    Returns dK, dV [keys, D] for the keys of vt below n.
+    """
+    n, d = q.shape
+    keys = slice(vt * T, min(n, (vt + 1) * T))
+    nk = keys.stop - keys.start
+    dk = np.zeros((nk, d))
+    dv = np.zeros((nk, d))
+    for u in np.nonzero(kept[:, vt])[0]:
+        rows = slice(u * T, min(n, (u + 1) * T))
+        lse, delta = stats[u] if stats is not None else row_stats(q, k, v, do, kept, T, scale, u)
+        p = np.exp(scale * (q[rows] @ k[keys].T) - lse[:, None])
+        dp = do[rows] @ v[keys].T
+        ds = p * (dp - delta[:, None])
+        dv += p.T @ do[rows]
+        dk += scale * (ds.T @ q[rows])
+    return dk, dv

@@ -67,6 +67,7 @@ def _declare(L):
         "radial_attn_bwd_workspace_bytes": (sz, [vp, i32, i32, i64, i32]),
         "radial_attn_bwd": (c.c_int, [vp, i32, i32, i64, i32, f32, vp, vp, vp, vp, vp, vp,
                                       vp, vp, vp, vp, sz, vp]),
+        "radial_test_set_fwd_group": (c.c_int, [i32]),
         "radial_status_string": (c.c_char_p, [c.c_int]),
         "radial_last_error": (c.c_char_p, []),
     }
@@ -283,8 +284,12 @@ def attn_bwd(q, k, v, o, lse, do, layout: Layout, scale: float | None = None,
     for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
         _check_qkv(name, t, None if name == "q" else q)
     B, H, N, D = q.shape
-    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N) or not lse.is_contiguous():
-        raise ValueError("lse must be contiguous fp32 [B, H, N]")
+    if (not lse.is_cuda or lse.device != q.device or lse.dtype != torch.float32
+            or tuple(lse.shape) != (B, H, N) or not lse.is_contiguous()):
+        raise ValueError("lse must be contiguous fp32 [B, H, N] on q's device")
+    if workspace is not None and (not workspace.is_cuda or workspace.device != q.device
+                                  or not workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous GPU tensor on q's device")
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     if out is None:
         dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)

@@ -41,7 +41,12 @@ def _run(cmd):
 
 def build(verbose: bool = False, defines=(), out: str = LIB) -> str:
     """Compile every source and link libradial.so (or `out`); returns its path.
-    `defines`: extra NAME=VALUE preprocessor definitions (tuning constants)."""
+    `defines`: extra NAME=VALUE preprocessor definitions (tuning constants).
+    `out` must name a ``.so`` file directly inside the package directory (the
+    library and its temporary copy are never written anywhere else)."""
+    out = os.path.abspath(out) if out else ""
+    if not out.endswith(".so") or os.path.dirname(out) != PKG:
+        raise ValueError(f"out must be a .so file in {PKG}, got {out!r}")
     if not os.path.exists(HIPCC):
         raise RuntimeError(f"hipcc not found at {HIPCC}")
     tmp = tempfile.mkdtemp(prefix="radial_build_")

@@ -204,11 +204,14 @@ __global__ __launch_bounds__(T / 32 * 64, 1) void radial_bwd_dkdv_kernel(
   constexpr int NPIECE = C::Copier::NDMA + 1;
   auto copy_piece = [&](int buf, int code, int half, int k) __attribute__((always_inline)) {
     const int m0 = code & 0x7fffffff;
+    // the resources cover this chunk's rows only (at most MC, so the byte
+    // counts stay small whatever N); rows at or past N read as zeros
+    const int rows = N - m0 < C::MC ? N - m0 : C::MC;
     if (k == 0) {
-      const u32x4 rl = rsrc_words((half ? NDelta : NLse2) + rbase + m0, (N - m0) * 4);
+      const u32x4 rl = rsrc_words((half ? NDelta : NLse2) + rbase + m0, rows * 4);
       dma4_async(rl, lds_r + buf * 2 * C::MC + half * C::MC, 4 * lane);
     } else {
-      const u32x4 rq = rsrc_words((half ? dOb : Qb) + (int64_t)m0 * D, (N - m0) * D * 2);
+      const u32x4 rq = rsrc_words((half ? dOb : Qb) + (int64_t)m0 * D, rows * D * 2);
       const int jj = k - 1;
       dma16_async(rq, (half ? lds_do : lds_q) + buf * C::CHUNK + (wave * C::Copier::NDMA + jj) * 512,
                   cp.off[jj]);

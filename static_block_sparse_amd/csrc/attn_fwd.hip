@@ -164,7 +164,10 @@ radial_fwd_kernel(const bf16 *__restrict__ Q, const bf16 *__restrict__ K,
   }
   auto issue_copy = [&](int buf, int k0) {
     if (!copier) return;
-    const int bytes = (N - k0) * D * 2;
+    // the resource covers this chunk's keys only (at most KC rows, so the
+    // byte count stays small whatever N); keys at or past N read as zeros
+    const int rows = N - k0 < C::KC ? N - k0 : C::KC;
+    const int bytes = rows * D * 2;
     const auto rk = make_rsrc(Kb + (int64_t)k0 * D, bytes);
     const auto rv = make_rsrc(Vb + (int64_t)k0 * D, bytes);
     bf16 *kd = lds + buf * C::BUF;

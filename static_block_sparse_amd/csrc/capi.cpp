@@ -3,6 +3,7 @@
 #include <hip/hip_runtime_api.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <cstdlib>
@@ -32,13 +33,9 @@ bool forced_alloc_failure() {
   return e && e[0] == '1';
 }
 
-// Query-tile grouping hook for tests: RADIAL_TEST_FWD_GROUP=1 or 2 caps the
-// forward's grouping (single tiles / pairs) so a test can compare the three
-// forms, which must agree bit for bit.  Unset: up to triples.
-int32_t forced_max_group() {
-  const char *e = std::getenv("RADIAL_TEST_FWD_GROUP");
-  return (e && (e[0] == '1' || e[0] == '2') && e[1] == 0) ? e[0] - '0' : 3;
-}
+// Largest query-tile group the forward uses (3: triples); lowered only by
+// radial_test_set_fwd_group, so tests can compare the three forms.
+std::atomic<int32_t> g_fwd_max_group{3};
 
 void free_device(radial_layout *L) {
   if (L->d_base) {
@@ -60,6 +57,11 @@ int check_common(const radial_layout *L, int32_t B, int32_t H, int64_t N, int32_
                  float scale) {
   if (!L) return fail(RADIAL_E_INVALID, "layout is NULL");
   if (B < 1 || H < 1) return fail(RADIAL_E_INVALID, "B and H must be >= 1");
+  // one (batch, head) slice must stay below 2^31 bytes: the kernels address
+  // rows within a slice with 32-bit offsets
+  if (N < 1 || (D > 0 && N > ((int64_t(1) << 31) - 1) / (2 * (int64_t)D)))
+    return fail(RADIAL_E_UNSUPPORTED, "N * D * 2 = " + std::to_string(N * 2 * (int64_t)D) +
+                                          " bytes per (batch, head); must be < 2^31");
   if (N != L->n)
     return fail(RADIAL_E_SHAPE, "N = " + std::to_string(N) + " but the layout has n = " +
                                     std::to_string(L->n) + " (frames * tokens_per_frame)");
@@ -303,7 +305,7 @@ int radial_attn_fwd(const radial_layout *L, int32_t B, int32_t H, int64_t N, int
   a.tri_idx = L->d_tri_idx;
   a.tri_tiles = L->d_tri_tiles;
   a.n_tri = static_cast<int32_t>(L->tri_tiles.size() / 3);
-  a.max_group = forced_max_group();
+  a.max_group = g_fwd_max_group.load(std::memory_order_relaxed);
   a.BH = B * H;
   a.N = static_cast<int32_t>(N);
   a.D = D;
@@ -378,6 +380,12 @@ int radial_attn_bwd(const radial_layout *L, int32_t B, int32_t H, int64_t N, int
   if (e != hipSuccess)
     return fail(RADIAL_E_HIP, std::string("backward launch failed: ") + hipGetErrorString(e));
   return RADIAL_OK;
+}
+
+int radial_test_set_fwd_group(int32_t max_group) {
+  if (max_group < 1 || max_group > 3)
+    return fail(RADIAL_E_INVALID, "max_group must be 1, 2 or 3");
+  return g_fwd_max_group.exchange(max_group);
 }
 
 const char *radial_status_string(int status) {

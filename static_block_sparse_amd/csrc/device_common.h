@@ -250,7 +250,10 @@ __device__ __forceinline__ void TileCopier<D, ROWS, NW>::init(int wave, int lane
 template <int D, int ROWS, int NW>
 __device__ __forceinline__ void TileCopier<D, ROWS, NW>::copy_async(bf16 *dst, const bf16 *src,
                                                                     int valid, int wave) const {
-  const u32x4 r = rsrc_words(src, valid * D * 2);
+  // the resource covers this tile's rows only (at most ROWS, so the byte
+  // count stays small whatever the sequence length)
+  const int rows = valid < ROWS ? valid : ROWS;
+  const u32x4 r = rsrc_words(src, rows * D * 2);
 #pragma unroll
   for (int jj = 0; jj < NDMA; ++jj) dma16_async(r, dst + (wave * NDMA + jj) * 512, off[jj]);
 }

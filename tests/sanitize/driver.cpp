@@ -170,7 +170,27 @@ int main() {
   EXPECT(radial_mask_build(8, 256, 64, RADIAL_SINK, &L2) == RADIAL_E_NOMEM && L2 == nullptr);
   unsetenv("RADIAL_TEST_FAIL_ALLOC");
   EXPECT(radial_layout_upload(L) == RADIAL_OK);
+  // slices of 2^31 bytes or more are refused before any launch (no buffer
+  // of that size exists here: a launch would touch the small blocks below
+  // far out of range)
+  {
+    const size_t x = 2048 * 128 * 2;
+    void *q = block(x), *k = block(x), *v = block(x), *o = block(x), *dout = block(x);
+    void *dq = block(x), *dk = block(x), *dv = block(x), *ws = block(1 << 16);
+    float *lse = static_cast<float *>(block(2048 * 4));
+    for (int64_t N : {int64_t(1) << 23, int64_t(1) << 30, int64_t(1) << 40}) {
+      EXPECT(radial_attn_fwd(L, 1, 1, N, 128, 0.1f, q, k, v, o, lse, nullptr) ==
+             RADIAL_E_UNSUPPORTED);
+      EXPECT(radial_attn_bwd(L, 1, 1, N, 128, 0.1f, q, k, v, o, lse, dout, dq, dk, dv, ws,
+                             1 << 16, nullptr) == RADIAL_E_UNSUPPORTED);
+    }
+    for (void *p : {q, k, v, o, dout, dq, dk, dv, ws, static_cast<void *>(lse)}) std::free(p);
+  }
   radial_layout_destroy(L);
+  // the forward's group cap
+  EXPECT(radial_test_set_fwd_group(0) == RADIAL_E_INVALID);
+  EXPECT(radial_test_set_fwd_group(2) == 3);
+  EXPECT(radial_test_set_fwd_group(3) == 2);
 
   // schedule decisions, status strings
   for (int l = 0; l < 4; ++l)

@@ -146,6 +146,7 @@ namespace radial {
 hipError_t launch_fwd(const FwdArgs &a, hipStream_t) {
   const size_t x = size_t(a.BH) * a.N * a.D * 2, r = size_t(a.BH) * a.N * 4;
   check(a.BH >= 1 && a.N >= 1 && a.nb == (a.N + a.T - 1) / a.T, "forward sizes");
+  check(int64_t(a.N) * a.D * 2 < (int64_t(1) << 31), "forward slice below 2^31 bytes");
   read_range(a.q, x);
   read_range(a.k, x);
   read_range(a.v, x);
@@ -165,6 +166,7 @@ hipError_t launch_fwd(const FwdArgs &a, hipStream_t) {
 hipError_t launch_bwd(const BwdArgs &a, hipStream_t) {
   const size_t x = size_t(a.BH) * a.N * a.D * 2, r = size_t(a.BH) * a.N * 4;
   check(a.BH >= 1 && a.N >= 1 && a.nb == (a.N + a.T - 1) / a.T, "backward sizes");
+  check(int64_t(a.N) * a.D * 2 < (int64_t(1) << 31), "backward slice below 2^31 bytes");
   for (const void *p : {a.q, a.k, a.v, a.o, a.dout}) read_range(p, x);
   read_range(a.lse, r);
   for (void *p : {a.dq, a.dk, a.dv}) write_range(p, x);

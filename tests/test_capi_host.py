@@ -254,6 +254,70 @@ def test_compute_calls_validate_before_touching_the_gpu():
     assert lib.radial_status_string(-3) == b"shape mismatch"
 
 
+def test_compute_calls_reject_slices_of_2_gib_or_more():
+    # one (batch, head) slice of N * D bf16 must stay below 2^31 bytes (the
+    # kernels address rows inside a slice with 32-bit offsets); the check
+    # runs before N is compared with the layout, so a small layout suffices
+    lib = sba.lib()
+    L = sba.Layout(8, 256, 64)
+    dummy = 4096
+    for N, D in ((1 << 23, 128), (1 << 24, 64), ((1 << 31) // 256, 128), (1 << 33, 128)):
+        fa = (L.handle, 1, 1, N, D, 0.125, dummy, dummy, dummy, dummy, dummy, None)
+        assert lib.radial_attn_fwd(*fa) == -2, (N, D)
+        assert "2^31" in lib.radial_last_error().decode()
+        ba = (L.handle, 1, 1, N, D, 0.125) + (dummy,) * 10 + (1 << 20, None)
+        assert lib.radial_attn_bwd(*ba) == -2, (N, D)
+    # the largest N below the limit only fails the layout comparison
+    N = (1 << 31) // 256 - 1
+    fa = (L.handle, 1, 1, N, 128, 0.125, dummy, dummy, dummy, dummy, dummy, None)
+    assert lib.radial_attn_fwd(*fa) == -3
+
+
+def test_forward_group_test_hook():
+    lib = sba.lib()
+    assert lib.radial_test_set_fwd_group(0) == -1
+    assert lib.radial_test_set_fwd_group(4) == -1
+    try:
+        assert lib.radial_test_set_fwd_group(1) == 3
+        assert lib.radial_test_set_fwd_group(2) == 1
+    finally:
+        assert lib.radial_test_set_fwd_group(3) in (1, 2, 3)
+
+
+def test_binding_rejects_host_tensors_before_any_launch():
+    # a CPU lse or workspace would hand a host pointer to the kernels; the
+    # binding refuses them with ValueError before calling the library
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("checks the CPU-side refusal only")
+    L = sba.Layout(8, 256, 64)
+
+    class FakeCuda:
+        """Stands in for a GPU bf16 tensor: passes the q/k/v checks only."""
+        is_cuda = True
+        dtype = torch.bfloat16
+        shape = torch.Size((1, 1, 2048, 64))
+        device = torch.device("cuda", 0)
+
+        def dim(self):
+            return 4
+
+        def is_contiguous(self):
+            return True
+
+    class FakeLse(FakeCuda):
+        dtype = torch.float32
+        shape = torch.Size((1, 1, 2048))
+
+    x = FakeCuda()
+    lse_cpu = torch.empty((1, 1, 2048), dtype=torch.float32)
+    with pytest.raises(ValueError, match="lse"):
+        sba.attn_bwd(x, x, x, x, lse_cpu, x, L)
+    ws_cpu = torch.empty(1 << 16, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="workspace"):
+        sba.attn_bwd(x, x, x, x, FakeLse(), x, L, workspace=ws_cpu)
+
+
 def test_allocation_failure_hook(monkeypatch):
     monkeypatch.setenv("RADIAL_TEST_FAIL_ALLOC", "1")
     h = ctypes.c_void_p()

@@ -2,11 +2,13 @@
 
 Small shapes: dQ, dK, dV compared element by element over every head.
 Full-size training workload (66 frames x 3600 tokens, 24 heads): dQ on
-sampled query tiles against the oracle, and dK, dV through identities that
-hold at any size: sum_n dV[n] = sum_m dO[m] (softmax rows sum to one) and
-sum_n dK[n] = 0 (each row of dS sums to zero).
+sampled query tiles and dK, dV on sampled key tiles (the sink column of the
+whole sequence included) element by element against the oracle, plus
+identities that hold at any size: sum_n dV[n] = sum_m dO[m] (softmax rows
+sum to one) and sum_n dK[n] = 0 (each row of dS sums to zero).
 """
 
+import os
 import sys
 
 import numpy as np
@@ -125,7 +127,11 @@ def test_backward_deterministic():
         assert torch.equal(x, y)
 
 
-def test_full_size_training_step():
+@pytest.fixture(scope="module")
+def full_training_step():
+    """The full-size training workload (66 frames x 3600 tokens, 24 heads,
+    D = 128) run forward and backward in bench's launch configuration (every
+    batch and head in one launch)."""
     w = workloads.WORKLOADS["train_f66"]
     _say(f"[bwd-full] {w.name} B={w.B} H={w.H} N={w.N} D={w.D}")
     q, k, v, do = workloads.workload_inputs(w, device="cuda")
@@ -133,19 +139,25 @@ def test_full_size_training_step():
     o, lse = sba.attn_fwd(q, k, v, L, w.scale)
     dq, dk, dv = sba.attn_bwd(q, k, v, o, lse, do, L, w.scale)
     torch.cuda.synchronize()
+    return dict(w=w, q=q, k=k, v=v, do=do, dq=dq, dk=dk, dv=dv)
+
+
+def test_full_size_training_step(full_training_step):
+    r = full_training_step
+    w, q, k, v, do, dq, dk, dv = (r[x] for x in ("w", "q", "k", "v", "do", "dq", "dk", "dv"))
     for t in (dq, dk, dv):
         assert bool(torch.isfinite(t.float()).all())
     # identities over every head
     sdv = dv.double().sum(dim=2)
     sdo = do.double().sum(dim=2)
     rms_dv = float(dv.double().pow(2).mean().sqrt())
-    # each of N bf16-rounded terms is off by <= 2^-9 relative: the sum's
-    # error grows like sqrt(N) * 2^-9 * rms
-    tol = 8 * np.sqrt(w.N) * 2.0 ** -9 * max(rms_dv, float(do.double().pow(2).mean().sqrt()))
+    # each of N bf16-rounded terms is off by <= 2^-8 relative (random
+    # signs): the sum's error grows like sqrt(N) * 2^-8 * rms; 4x margin
+    tol = 4 * np.sqrt(w.N) * 2.0 ** -8 * max(rms_dv, float(do.double().pow(2).mean().sqrt()))
     assert float((sdv - sdo).abs().max()) <= tol, (float((sdv - sdo).abs().max()), tol)
     sdk = dk.double().sum(dim=2)
     rms_dk = float(dk.double().pow(2).mean().sqrt())
-    assert float(sdk.abs().max()) <= 8 * np.sqrt(w.N) * 2.0 ** -9 * rms_dk + 1e-6
+    assert float(sdk.abs().max()) <= 4 * np.sqrt(w.N) * 2.0 ** -8 * rms_dk + 1e-6
     # dQ on sampled query tiles of the first and last heads
     kept = om.kept_tiles(w.frames, w.tokens_per_frame, w.T, True)
     for h in (0, w.H - 1):
@@ -154,3 +166,49 @@ def test_full_size_training_step():
             rows = slice(u * w.T, min(w.N, (u + 1) * w.T))
             rq = oa.bwd_dq_tile(qh, kh, vh, dh, kept, w.T, w.scale, u)
             check_close(f64(dq[0, h, rows]), rq, f"dQ h={h} tile={u}", normalise=True)
+
+
+@pytest.mark.timeout(900)
+def test_full_size_dkdv_tiles(full_training_step):
+    """dK and dV element by element at the full training workload, on key
+    tiles whose CSC columns take every path of the dK/dV walk: tile 0 (the
+    sink: every query tile of the sequence attends it, 1857 of them), tile
+    28 (straddles frames 0 and 1), the last, partial key tile (16 valid
+    keys) and one random tile of the first head, and the last tile of the
+    last head.  The oracle takes each row's full softmax over its own kept
+    keys, so the sink columns need the row terms of the whole head."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    from threadpoolctl import threadpool_limits
+
+    r = full_training_step
+    w, q, k, v, do, dk, dv = (r[x] for x in ("w", "q", "k", "v", "do", "dk", "dv"))
+    kept = om.kept_tiles(w.frames, w.tokens_per_frame, w.T, True)
+    nb = kept.shape[0]
+    frame0_tiles = -(-w.tokens_per_frame // w.T)  # 29: tile 28 straddles frames 0 and 1
+    rand = int(np.random.default_rng(7).integers(frame0_tiles, nb - 1))
+    cases = {0: [0, frame0_tiles - 1, nb - 1, rand], w.H - 1: [nb - 1]}
+    workers = min(16, os.cpu_count() or 1)
+    for h, tiles in cases.items():
+        qh, kh, vh, dh = f64(q[0, h]), f64(k[0, h]), f64(v[0, h]), f64(do[0, h])
+        need = sorted(set(int(u) for vt in tiles for u in np.nonzero(kept[:, vt])[0]))
+        _say(f"[dkdv-full] head {h}: key tiles {tiles}, row terms of {len(need)} query tiles "
+             f"on {workers} threads")
+
+        def stats_of(u):
+            return u, oa.row_stats(qh, kh, vh, dh, kept, w.T, w.scale, u)
+
+        stats = {}
+        with threadpool_limits(1), ThreadPoolExecutor(workers) as ex:
+            for i, (u, st) in enumerate(ex.map(stats_of, need)):
+                stats[u] = st
+                if (i + 1) % 400 == 0:
+                    _say(f"[dkdv-full]   {i + 1} of {len(need)}")
+        for vt in tiles:
+            keys = slice(vt * w.T, min(w.N, (vt + 1) * w.T))
+            rk, rv = oa.bwd_dkdv_tile(qh, kh, vh, dh, kept, w.T, w.scale, vt, stats=stats)
+            sk = check_close(f64(dk[0, h, keys]), rk, f"dK h={h} key tile={vt}", normalise=True)
+            sv = check_close(f64(dv[0, h, keys]), rv, f"dV h={h} key tile={vt}", normalise=True)
+            _say(f"[dkdv-full] head {h} key tile {vt} (column of {int(kept[:, vt].sum())}): "
+                 f"dK max {sk['max_abs']:.3g} (rms {sk['rms_ref']:.3g}), "
+                 f"dV max {sv['max_abs']:.3g} (rms {sv['rms_ref']:.3g})")

@@ -131,10 +131,10 @@ def test_exact_full_size_sampled_rows():
             check_close(f64(dq[0, h, rows]), rq, f"dQ h={h} tile={u}", normalise=True)
     # every softmax row sums to one: sum_n dV[n] = sum_m dO[m]; each dS row
     # sums to zero: sum_n dK[n] = 0.  Each of N bf16-rounded terms is off by
-    # <= 2^-9 relative, so the sums' errors grow like sqrt(N) * 2^-9 * rms.
+    # <= 2^-8 relative, so the sums' errors grow like sqrt(N) * 2^-8 * rms (4x margin).
     sdv, sdo = dv.double().sum(dim=2), do.double().sum(dim=2)
     rms = max(float(dv.double().pow(2).mean().sqrt()), float(do.double().pow(2).mean().sqrt()))
-    tol = 8 * np.sqrt(w.N) * 2.0 ** -9 * rms
+    tol = 4 * np.sqrt(w.N) * 2.0 ** -8 * rms
     assert float((sdv - sdo).abs().max()) <= tol, (float((sdv - sdo).abs().max()), tol)
     rms_dk = float(dk.double().pow(2).mean().sqrt())
-    assert float(dk.double().sum(dim=2).abs().max()) <= 8 * np.sqrt(w.N) * 2.0 ** -9 * rms_dk + 1e-6
+    assert float(dk.double().sum(dim=2).abs().max()) <= 4 * np.sqrt(w.N) * 2.0 ** -8 * rms_dk + 1e-6

@@ -153,3 +153,51 @@ def test_dq_tile_matches_full_backward():
         rows = slice(u * T, min(n, (u + 1) * T))
         np.testing.assert_allclose(oa.bwd_dq_tile(q, k, v, do, kept, T, 0.7, u), dq[rows],
                                    rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("f,s,T,sink", [(6, 11, 8, True), (5, 30, 16, False), (9, 7, 4, True),
+                                        (3, 40, 64, True)])
+def test_dkdv_tile_matches_full_backward(f, s, T, sink):
+    # per key tile, from each row's own full softmax (the column's query
+    # tiles only), against the whole-head backward and, independently,
+    # torch float64 autograd of the masked softmax under the tile map
+    n, d = f * s, 5
+    q, k, v, do = (_rand((n, d), 70 + i) for i in range(4))
+    kept = om.kept_tiles(f, s, T, sink)
+    nb = kept.shape[0]
+    scale = 0.6
+    _, dk, dv = oa.bwd(q, k, v, do, kept, T, scale)
+    tq, tk, tv = (torch.from_numpy(x.copy()).requires_grad_() for x in (q, k, v))
+    tok = np.repeat(np.repeat(kept, T, axis=0), T, axis=1)[:n, :n]
+    z = scale * tq @ tk.T
+    z = z.masked_fill(~torch.from_numpy(tok), float("-inf"))
+    (torch.softmax(z, dim=1) @ tv).backward(torch.from_numpy(do))
+    stats = {u: oa.row_stats(q, k, v, do, kept, T, scale, u) for u in range(nb)}
+    for vt in range(nb):
+        keys = slice(vt * T, min(n, (vt + 1) * T))
+        gk, gv = oa.bwd_dkdv_tile(q, k, v, do, kept, T, scale, vt)
+        np.testing.assert_allclose(gk, dk[keys], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(gv, dv[keys], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(gk, tk.grad.numpy()[keys], rtol=0, atol=1e-11)
+        np.testing.assert_allclose(gv, tv.grad.numpy()[keys], rtol=0, atol=1e-11)
+        hk, hv = oa.bwd_dkdv_tile(q, k, v, do, kept, T, scale, vt, stats=stats)
+        np.testing.assert_array_equal(hk, gk)
+        np.testing.assert_array_equal(hv, gv)
+
+
+def test_row_stats_are_the_row_terms():
+    # LSE from the forward and Delta = rowsum(P * dP), the textbook form
+    f, s, T, d = 5, 13, 8, 3
+    n = f * s
+    q, k, v, do = (_rand((n, d), 80 + i) for i in range(4))
+    kept = om.kept_tiles(f, s, T, True)
+    _, lse_all = oa.fwd(q, k, v, kept, T, 0.9)
+    for u in range(kept.shape[0]):
+        rows = slice(u * T, min(n, (u + 1) * T))
+        cols = oa.tile_columns(kept[u], n, T)
+        z = 0.9 * q[rows] @ k[cols].T
+        p = np.exp(z - lse_all[rows, None])
+        lse, delta = oa.row_stats(q, k, v, do, kept, T, 0.9, u)
+        np.testing.assert_allclose(lse, lse_all[rows], rtol=0, atol=1e-13)
+        np.testing.assert_allclose(delta, (p * (do[rows] @ v[cols].T)).sum(axis=1),
+                                   rtol=0, atol=1e-12)

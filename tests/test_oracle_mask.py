@@ -7,6 +7,7 @@ symmetry and the halving of amortised density per band.
 """
 
 import math
+from fractions import Fraction
 import os
 
 import numpy as np
@@ -128,19 +129,37 @@ def test_single_token_frames_give_power_of_two_distances():
     assert dists == [0, 1, 2, 4, 8, 16, 32]
 
 
-def test_amortised_density_halves_below_unit_width():
-    # review Step 2-C: below unit width the diagonal is kept in a subsample
-    # of frame pairs so that the amortised density keeps halving per band.
-    # For s a power of two, over a whole band r (2**r >= s) the kept share of
-    # frame pairs times the diagonal density 1/s is exactly 2**-r.
-    for s in [1, 2, 4, 8]:
-        for r in range(int(math.log2(s)), 12):
-            kept = [d for d in range(2 ** r, 2 ** (r + 1))
-                    if om.band(d, s)[1] >= 1 or d % om.band(d, s)[2] == 0]
-            frac = len(kept) / 2 ** r
-            if om.band(2 ** r, s)[1] >= 1:
-                continue  # w >= 1: not the sampled regime
-            assert frac / s == pytest.approx(2.0 ** -r)
+@pytest.mark.parametrize("s", [3, 5, 6, 7])
+def test_sampled_bands_keep_the_halving_density(s):
+    # review Step 2-C (paper Fig.5 caption): once a band's width falls below
+    # one token, only the diagonal is kept, on a subsample of frame pairs
+    # chosen so the band's amortised density keeps the decay of the bands
+    # above it, 2^-r.  Read off the brute-force mask at sizes where s is not
+    # a power of two (so ceil and floor of 2^r / s differ): every frame-pair
+    # block of a sampled band is empty or exactly the diagonal, and the mean
+    # density over the band's distances lies in (2^-r / 2, 2^-r].  A
+    # subsample that keeps too many distances (a floor instead of the
+    # ceiling, say) breaks the upper bound; one that keeps too few breaks
+    # the lower.
+    f = 128 if s <= 5 else 256
+    m = om.token_mask(f, s, sink=False)
+    eye = np.eye(s, dtype=bool)
+    checked = 0
+    for r in range(1, 8):
+        lo, hi = 2 ** r, 2 ** (r + 1)
+        if lo <= s or hi > f:
+            continue  # width >= 1 there, or the band does not fit
+        dens = []
+        for d in range(lo, hi):
+            for i, j in ((0, d), (d, 0), (f - 1 - d, f - 1)):
+                blk = m[i * s:(i + 1) * s, j * s:(j + 1) * s]
+                assert not blk.any() or np.array_equal(blk, eye), (s, d, i, j)
+            dens.append(int(m[0:s, d * s:(d + 1) * s].sum()))
+        kept = sum(1 for x in dens if x > 0)
+        mean = Fraction(kept, s * (hi - lo))  # each kept block holds s of s^2 pairs
+        assert Fraction(1, 2 ** (r + 1)) < mean <= Fraction(1, 2 ** r), (s, r, mean)
+        checked += 1
+    assert checked >= 3
 
 
 def test_mask_symmetric_without_sink():
