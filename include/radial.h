@@ -234,6 +234,31 @@ int radial_attn_bwd(const radial_layout *L, int32_t B, int32_t H, int64_t N, int
                     const float *lse, const void *dout, void *dq, void *dk, void *dv,
                     void *workspace, size_t workspace_bytes, void *hip_stream);
 
+/* Bytes of the static device scratch radial_attn_bwd_noalloc uses (per
+   device, held until the process ends): room for the two row arrays at
+   B * H * N up to 8,388,544. */
+#define RADIAL_BWD_SCRATCH_BYTES ((size_t)64 << 20)
+
+/*
+ * radial_attn_bwd_noalloc -- radial_attn_bwd without a workspace argument,
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving or training loops, harnesses that forbid
+ * hipMalloc).  The two row arrays live in a static device array of
+ * RADIAL_BWD_SCRATCH_BYTES bytes that the library holds on every device it
+ * runs on; the call allocates nothing (the array's address is looked up on
+ * the first call on each device).  Same arguments, kernels and results as
+ * radial_attn_bwd (bit for bit).  RADIAL_E_UNSUPPORTED when
+ * radial_attn_bwd_workspace_bytes(L, B, H, N, D) > RADIAL_BWD_SCRATCH_BYTES.
+ * Every call on a device shares that device's scratch: calls that overlap
+ * in time on one device (different streams, threads) race and must be
+ * serialised by the caller.  Nothing in the scratch needs to start at zero:
+ * each call writes every row before reading it.
+ */
+int radial_attn_bwd_noalloc(const radial_layout *L, int32_t B, int32_t H, int64_t N, int32_t D,
+                            float scale, const void *q, const void *k, const void *v,
+                            const void *o, const float *lse, const void *dout, void *dq,
+                            void *dk, void *dv, void *hip_stream);
+
 /* Test hook: caps the query-tile grouping of every later radial_attn_fwd
    call in the process at max_group tiles per workgroup (1 single tiles, 2
    pairs, 3 triples, the default); the three forms give identical bits, and

@@ -20,7 +20,7 @@ import os
 
 import numpy as np
 
-__all__ = ["Layout", "Schedule", "attn_fwd", "attn_bwd", "lib", "LIB_PATH", "SINK", "DENSE",
+__all__ = ["Layout", "Schedule", "attn_fwd", "attn_bwd", "attn_bwd_noalloc", "lib", "LIB_PATH", "SINK", "DENSE",
            "TOKEN_EXACT", "DECAYS", "RadialError"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libradial.so")
@@ -67,6 +67,8 @@ def _declare(L):
         "radial_attn_bwd_workspace_bytes": (sz, [vp, i32, i32, i64, i32]),
         "radial_attn_bwd": (c.c_int, [vp, i32, i32, i64, i32, f32, vp, vp, vp, vp, vp, vp,
                                       vp, vp, vp, vp, sz, vp]),
+        "radial_attn_bwd_noalloc": (c.c_int, [vp, i32, i32, i64, i32, f32, vp, vp, vp, vp, vp,
+                                              vp, vp, vp, vp, vp]),
         "radial_test_set_fwd_group": (c.c_int, [i32]),
         "radial_status_string": (c.c_char_p, [c.c_int]),
         "radial_last_error": (c.c_char_p, []),
@@ -308,4 +310,33 @@ def attn_bwd(q, k, v, o, lse, do, layout: Layout, scale: float | None = None,
                                      v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
                                      dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws.data_ptr(),
                                      ws.numel() * ws.element_size(), stream))
+    return dq, dk, dv
+
+
+def attn_bwd_noalloc(q, k, v, o, lse, do, layout: Layout, scale: float | None = None, out=None):
+    """``attn_bwd`` through radial_attn_bwd_noalloc: the library keeps the
+    backward's row arrays in its static device scratch instead of a
+    workspace (nothing is allocated when ``out`` is given).  Same results,
+    bit for bit.  Calls that overlap on one device race on the scratch."""
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
+        _check_qkv(name, t, None if name == "q" else q)
+    B, H, N, D = q.shape
+    if (not lse.is_cuda or lse.device != q.device or lse.dtype != torch.float32
+            or tuple(lse.shape) != (B, H, N) or not lse.is_contiguous()):
+        raise ValueError("lse must be contiguous fp32 [B, H, N] on q's device")
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    if out is None:
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    else:
+        dq, dk, dv = out
+        for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+            _check_qkv(name, t, q)
+    layout.upload(q.device)
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        _check(lib().radial_attn_bwd_noalloc(layout.handle, B, H, N, D, scale, q.data_ptr(),
+                                             k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                             lse.data_ptr(), do.data_ptr(), dq.data_ptr(),
+                                             dk.data_ptr(), dv.data_ptr(), stream))
     return dq, dk, dv

@@ -21,6 +21,8 @@
 // gfx950 transposing LDS load, so each operand is staged once.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -772,6 +774,30 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t stream) {
                         : launch_bwd_t<D, T, false, true>(a, stream);
   return a.mask.exact ? launch_bwd_t<D, T, true, false>(a, stream)
                       : launch_bwd_t<D, T, false, false>(a, stream);
+}
+
+// Static scratch for the allocation-free backward entry point: the two
+// fp32 row arrays (-Delta, -LSE log2(e)) that radial_attn_bwd keeps in its
+// caller's workspace.  Each device holds its own copy at its own address;
+// host code uses only the addresses bwd_scratch looks up (the array's name
+// is a host-side stand-in, not a device address).
+static __device__ __align__(256) unsigned char scratch[kBwdScratchBytes];
+
+hipError_t bwd_scratch(int device, void **ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void *addr[kMaxDevices] = {};
+  if (!ptr || device < 0 || device >= kMaxDevices) return hipErrorInvalidValue;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[device]) {
+    void *p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[device] = p;
+  }
+  *ptr = addr[device];
+  return hipSuccess;
 }
 
 hipError_t launch_bwd(const BwdArgs &a, hipStream_t stream) {

@@ -15,6 +15,8 @@
 #include "layout.h"
 #include "radial.h"
 
+static_assert(radial::kBwdScratchBytes == RADIAL_BWD_SCRATCH_BYTES, "scratch size");
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -329,27 +331,16 @@ size_t radial_attn_bwd_workspace_bytes(const radial_layout *L, int32_t B, int32_
   return 2 * ((bytes + 255) & ~size_t(255));
 }
 
-int radial_attn_bwd(const radial_layout *L, int32_t B, int32_t H, int64_t N, int32_t D,
-                    float scale, const void *q, const void *k, const void *v, const void *o,
-                    const float *lse, const void *dout, void *dq, void *dk, void *dv,
-                    void *workspace, size_t workspace_bytes, void *hip_stream) {
-  int st = check_common(L, B, H, N, D, scale);
-  if (st) return st;
-  st = check_ptrs({{q, "q"},
-                   {k, "k"},
-                   {v, "v"},
-                   {o, "o"},
-                   {lse, "lse"},
-                   {dout, "dout"},
-                   {dq, "dq"},
-                   {dk, "dk"},
-                   {dv, "dv"},
-                   {workspace, "workspace"}});
-  if (st) return st;
-  const size_t need = radial_attn_bwd_workspace_bytes(L, B, H, N, D);
-  if (workspace_bytes < need)
-    return fail(RADIAL_E_INVALID, "workspace too small: need " + std::to_string(need) +
-                                      " bytes, got " + std::to_string(workspace_bytes));
+}  // extern "C"
+
+namespace {
+
+// The backward's launches once every argument has been checked; `workspace`
+// holds `need` bytes (the two row arrays, need / 2 bytes each).
+int run_bwd(const radial_layout *L, int32_t B, int32_t H, int64_t N, int32_t D, float scale,
+            const void *q, const void *k, const void *v, const void *o, const float *lse,
+            const void *dout, void *dq, void *dk, void *dv, void *workspace, size_t need,
+            void *hip_stream) {
   radial::BwdArgs a;
   a.q = q;
   a.k = k;
@@ -380,6 +371,67 @@ int radial_attn_bwd(const radial_layout *L, int32_t B, int32_t H, int64_t N, int
   if (e != hipSuccess)
     return fail(RADIAL_E_HIP, std::string("backward launch failed: ") + hipGetErrorString(e));
   return RADIAL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int radial_attn_bwd(const radial_layout *L, int32_t B, int32_t H, int64_t N, int32_t D,
+                    float scale, const void *q, const void *k, const void *v, const void *o,
+                    const float *lse, const void *dout, void *dq, void *dk, void *dv,
+                    void *workspace, size_t workspace_bytes, void *hip_stream) {
+  int st = check_common(L, B, H, N, D, scale);
+  if (st) return st;
+  st = check_ptrs({{q, "q"},
+                   {k, "k"},
+                   {v, "v"},
+                   {o, "o"},
+                   {lse, "lse"},
+                   {dout, "dout"},
+                   {dq, "dq"},
+                   {dk, "dk"},
+                   {dv, "dv"},
+                   {workspace, "workspace"}});
+  if (st) return st;
+  const size_t need = radial_attn_bwd_workspace_bytes(L, B, H, N, D);
+  if (workspace_bytes < need)
+    return fail(RADIAL_E_INVALID, "workspace too small: need " + std::to_string(need) +
+                                      " bytes, got " + std::to_string(workspace_bytes));
+  return run_bwd(L, B, H, N, D, scale, q, k, v, o, lse, dout, dq, dk, dv, workspace, need,
+                 hip_stream);
+}
+
+int radial_attn_bwd_noalloc(const radial_layout *L, int32_t B, int32_t H, int64_t N, int32_t D,
+                            float scale, const void *q, const void *k, const void *v,
+                            const void *o, const float *lse, const void *dout, void *dq,
+                            void *dk, void *dv, void *hip_stream) {
+  int st = check_common(L, B, H, N, D, scale);
+  if (st) return st;
+  st = check_ptrs({{q, "q"},
+                   {k, "k"},
+                   {v, "v"},
+                   {o, "o"},
+                   {lse, "lse"},
+                   {dout, "dout"},
+                   {dq, "dq"},
+                   {dk, "dk"},
+                   {dv, "dv"}});
+  if (st) return st;
+  const size_t need = radial_attn_bwd_workspace_bytes(L, B, H, N, D);
+  if (need > radial::kBwdScratchBytes)
+    return fail(RADIAL_E_UNSUPPORTED,
+                "B * H * N too large for the static scratch: the row arrays need " +
+                    std::to_string(need) + " bytes, the scratch holds " +
+                    std::to_string(radial::kBwdScratchBytes) + " (RADIAL_BWD_SCRATCH_BYTES)");
+  // check_common made sure the layout's device is the current one
+  void *scratch = nullptr;
+  const hipError_t e = radial::bwd_scratch(L->device, &scratch);
+  if (e != hipSuccess)
+    return fail(RADIAL_E_HIP, std::string("static scratch lookup failed: ") +
+                                  hipGetErrorString(e));
+  return run_bwd(L, B, H, N, D, scale, q, k, v, o, lse, dout, dq, dk, dv, scratch, need,
+                 hip_stream);
 }
 
 int radial_test_set_fwd_group(int32_t max_group) {

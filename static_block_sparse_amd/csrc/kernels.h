@@ -77,4 +77,14 @@ struct BwdArgs {
 hipError_t launch_fwd(const FwdArgs &a, hipStream_t stream);
 hipError_t launch_bwd(const BwdArgs &a, hipStream_t stream);
 
+// Size of the backward's static device scratch (attn_bwd.hip): room for the
+// two fp32 row arrays of radial_attn_bwd's workspace at B * H * N rows up to
+// about 8.4 million.  Held by every device the library runs on until the
+// process ends.
+constexpr size_t kBwdScratchBytes = size_t(64) << 20;
+
+// Device address of the backward's static scratch array on `device`, which
+// must be the current device: looked up once per device, then cached.
+hipError_t bwd_scratch(int device, void **ptr);
+
 }  // namespace radial

@@ -74,6 +74,8 @@ void exercise(const Shape &sh) {
   const float sc = 0.125f;
   EXPECT(radial_attn_fwd(L, B, H, n, D, sc, q, k, v, o, lse, nullptr) ==
          (supported ? RADIAL_E_STATE : RADIAL_E_UNSUPPORTED));
+  EXPECT(radial_attn_bwd_noalloc(L, B, H, n, D, sc, q, k, v, o, lse, dout, dq, dk, dv, nullptr) ==
+         (supported ? RADIAL_E_STATE : RADIAL_E_UNSUPPORTED));
 
   EXPECT(radial_layout_upload(L) == RADIAL_OK);
   EXPECT(radial_layout_upload(L) == RADIAL_OK);  // second upload: no-op
@@ -86,6 +88,11 @@ void exercise(const Shape &sh) {
                            nullptr) == RADIAL_OK);
     EXPECT(radial_attn_bwd(L, B, H, n, D, sc, q, k, v, o, lse, dout, dq, dk, dv, ws,
                            ws_bytes - 1, nullptr) == RADIAL_E_INVALID);
+    // the allocation-free variant: the same launches on the static scratch
+    EXPECT(radial_attn_bwd_noalloc(L, B, H, n, D, sc, q, k, v, o, lse, dout, dq, dk, dv,
+                                   nullptr) == RADIAL_OK);
+    EXPECT(radial_attn_bwd_noalloc(L, B, H, n, D, sc, q, k, v, o, lse, dout, dq, dk, nullptr,
+                                   nullptr) == RADIAL_E_INVALID);
     // misaligned and missing pointers, wrong sizes
     EXPECT(radial_attn_fwd(L, B, H, n, D, sc, static_cast<char *>(q) + 2, k, v, o, lse,
                            nullptr) == RADIAL_E_INVALID);
@@ -185,6 +192,17 @@ int main() {
                              1 << 16, nullptr) == RADIAL_E_UNSUPPORTED);
     }
     for (void *p : {q, k, v, o, dout, dq, dk, dv, ws, static_cast<void *>(lse)}) std::free(p);
+  }
+  {
+    // the allocation-free backward refuses row arrays beyond its scratch
+    // (B * H * n = 4100 * 2048 rows: 67.2 MB) before touching any pointer
+    const size_t x = 64;
+    void *p = block(x);
+    const float *lp = static_cast<const float *>(p);
+    EXPECT(radial_attn_bwd_workspace_bytes(L, 1, 4100, 2048, 64) > RADIAL_BWD_SCRATCH_BYTES);
+    EXPECT(radial_attn_bwd_noalloc(L, 1, 4100, 2048, 64, 0.1f, p, p, p, p, lp, p, p, p, p,
+                                   nullptr) == RADIAL_E_UNSUPPORTED);
+    std::free(p);
   }
   radial_layout_destroy(L);
   // the forward's group cap

@@ -188,4 +188,13 @@ hipError_t launch_bwd(const BwdArgs &a, hipStream_t) {
   return hipSuccess;
 }
 
+// the static scratch: a heap block of the stated size, looked up per device
+hipError_t bwd_scratch(int device, void **ptr) {
+  static void *block = nullptr;
+  check(device == 0, "scratch looked up on the current device");
+  if (!block) block = std::malloc(kBwdScratchBytes);
+  *ptr = block;
+  return block ? hipSuccess : hipErrorOutOfMemory;
+}
+
 }  // namespace radial

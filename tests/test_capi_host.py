@@ -252,6 +252,13 @@ def test_compute_calls_validate_before_touching_the_gpu():
     b = (L.handle, 1, 1, 2000, 64, 0.125) + (dummy,) * 10 + (ws, None)
     assert lib.radial_attn_bwd(*b) == -3
     assert lib.radial_status_string(-3) == b"shape mismatch"
+    # the allocation-free backward validates the same way
+    nb_ = (L.handle, 1, 1, 2048, 64, 0.125) + (dummy,) * 9 + (None,)
+    assert lib.radial_attn_bwd_noalloc(*nb_) == -6
+    nb_ = (None, 1, 1, 2048, 64, 0.125) + (dummy,) * 9 + (None,)
+    assert lib.radial_attn_bwd_noalloc(*nb_) == -1
+    nb_ = (L.handle, 1, 1, 2048, 64, 0.125) + (dummy,) * 8 + (None, None)
+    assert lib.radial_attn_bwd_noalloc(*nb_) in (-1, -6)
 
 
 def test_compute_calls_reject_slices_of_2_gib_or_more():
