@@ -146,7 +146,11 @@ radial_fwd_kernel(const bf16 *__restrict__ Q, const bf16 *__restrict__ K,
   auto chunk_raw = [&](int c) { return lidx[t_begin + c / C::CPT]; };
   auto key_of = [&](int raw, int c) { return (raw & TMASK) * T + (c % C::CPT) * C::KC; };
   // this lane's query as (frame, position), for the token predicate
-  const int qi = qrow / mg.s, qa = qrow - (qrow / mg.s) * mg.s;
+  // (computed where a partial chunk needs it, from the wave's scalar tile
+  // and row offsets and the lane index, so nothing stays live across the
+  // chunk loop: with triples every register is taken, and values kept live
+  // there were spilled and reloaded inside the loop)
+  const int qrow0 = u * T + (wave % C::NWR) * 32;  // wave-uniform
 
   // Chunk staging by direct global -> LDS copies (no staging registers):
   // copy jj of copying wave w (w < NCW) fills LDS bytes
@@ -262,6 +266,9 @@ radial_fwd_kernel(const bf16 *__restrict__ Q, const bf16 *__restrict__ K,
             if (kb * 32 + 8 * (r >> 2) + (r & 3) >= lim) s[kb][r] = -INFINITY;
       }
       if (partial) {  // token-exact: keys outside the query's runs get -inf
+        const unsigned lid = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+        const int qr = qrow0 + (int)(lid & 31u);  // this lane's query row
+        const int qi = bctx.div_s(qr), qa = qr - qi * bctx.s;
         const unsigned ok = lane_key_bits<C::NKB>(bctx, qi, qa, key0, g);
         if (__ballot(ok != ~0u)) {  // some key of the wave's block is masked
 #pragma unroll
