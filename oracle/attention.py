@@ -44,6 +44,16 @@ def _softmax_rows(z: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
     return p, lse
 
 
+def fwd_rows(q_rows: np.ndarray, k_cols: np.ndarray, v_cols: np.ndarray,
+             scale: float) -> tuple[np.ndarray, np.ndarray]:
+    """O and LSE of some query rows over the keys they may attend: q_rows
+    float64 [r, D] and the attended keys' K and V rows k_cols, v_cols
+    float64 [c, D] (the definition, for rows whose allowed keys are given)."""
+    z = scale * (q_rows @ k_cols.T)
+    p, lse = _softmax_rows(z)
+    return p @ v_cols, lse
+
+
 def fwd_tile(q: np.ndarray, k: np.ndarray, v: np.ndarray, kept: np.ndarray,
              T: int, scale: float, u: int) -> tuple[np.ndarray, np.ndarray]:
     """O and LSE for the query rows of tile u of one (batch, head).
@@ -54,9 +64,7 @@ def fwd_tile(q: np.ndarray, k: np.ndarray, v: np.ndarray, kept: np.ndarray,
     n = q.shape[0]
     rows = slice(u * T, min(n, (u + 1) * T))
     cols = tile_columns(kept[u], n, T)
-    z = scale * (q[rows] @ k[cols].T)
-    p, lse = _softmax_rows(z)
-    return p @ v[cols], lse
+    return fwd_rows(q[rows], k[cols], v[cols], scale)
 
 
 def fwd(q: np.ndarray, k: np.ndarray, v: np.ndarray, kept: np.ndarray,
@@ -119,19 +127,25 @@ def bwd_masked(q, k, v, do, mask, scale):
     return scale * (ds @ k), scale * (ds.T @ q), p.T @ do
 
 
+def dq_rows(q_rows: np.ndarray, k_cols: np.ndarray, v_cols: np.ndarray,
+            do_rows: np.ndarray, scale: float) -> np.ndarray:
+    """dQ of some query rows over the keys they may attend (as ``fwd_rows``):
+    a query row's gradient depends only on its own softmax row."""
+    z = scale * (q_rows @ k_cols.T)
+    p, _ = _softmax_rows(z)
+    dp = do_rows @ v_cols.T
+    delta = (p * dp).sum(axis=1, keepdims=True)
+    return scale * ((p * (dp - delta)) @ k_cols)
+
+
 def bwd_dq_tile(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray,
                 kept: np.ndarray, T: int, scale: float, u: int) -> np.ndarray:
     """dQ for the valid rows of query tile u only (same formulas as ``bwd``,
-    restricted to one row block: a query row's gradient depends only on its
-    own softmax row)."""
+    restricted to one row block)."""
     n = q.shape[0]
     rows = slice(u * T, min(n, (u + 1) * T))
     cols = tile_columns(kept[u], n, T)
-    z = scale * (q[rows] @ k[cols].T)
-    p, _ = _softmax_rows(z)
-    dp = do[rows] @ v[cols].T
-    delta = (p * dp).sum(axis=1, keepdims=True)
-    return scale * ((p * (dp - delta)) @ k[cols])
+    return dq_rows(q[rows], k[cols], v[cols], do[rows], scale)
 
 
 def row_stats(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray,

@@ -199,7 +199,7 @@ def n_blocks(n: int, T: int) -> int:
 
 
 def kept_tiles(f: int, s: int, T: int, sink: bool = True,
-               variant: Variant = DEFAULT) -> np.ndarray:
+               variant: Variant = DEFAULT, tiles=None) -> np.ndarray:
     """Boolean [nb, nb] tile map: kept[u, v] iff some allowed (q, k) has
     q // T == u and k // T == v.
 
@@ -208,14 +208,27 @@ def kept_tiles(f: int, s: int, T: int, sink: bool = True,
     (|a - b| < w, or the single b == a, or all of frame 0 for the sink), so
     they cover a contiguous run of key tiles.  Each run is marked in a
     per-query-tile difference array and a prefix sum gives the union.
+
+    ``tiles``: optional list of query tiles; the sweep then covers only their
+    query tokens and the result has one row per listed tile,
+    [len(tiles), nb] (for sequences whose full map would not fit in memory).
     """
     n = f * s
     nb = n_blocks(n, T)
     tab = band_table(f, s, variant)
-    qtok = np.arange(n, dtype=np.int64)
+    if tiles is None:
+        qtok = np.arange(n, dtype=np.int64)
+        qtile = qtok // T
+        n_rows = nb
+    else:
+        tiles = [int(u) for u in tiles]
+        qtok = np.concatenate([np.arange(u * T, min(n, (u + 1) * T), dtype=np.int64)
+                               for u in tiles])
+        qtile = np.concatenate([np.full(min(n, (u + 1) * T) - u * T, r, dtype=np.int64)
+                                for r, u in enumerate(tiles)])
+        n_rows = len(tiles)
     qi, qa = np.divmod(qtok, s)
-    qtile = qtok // T
-    cover = np.zeros((nb, nb + 1), dtype=np.int64)
+    cover = np.zeros((n_rows, nb + 1), dtype=np.int64)
     flat = cover.reshape(-1)
     starts: list[np.ndarray] = []
     ends: list[np.ndarray] = []

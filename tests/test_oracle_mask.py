@@ -256,3 +256,16 @@ def test_token_mask_rows_matches_token_mask():
     rows = np.array([0, 5, 16, 77, 143])
     assert np.array_equal(om.token_mask_rows(f, s, rows, True), tok[rows])
     assert np.array_equal(om.token_mask_rows(f, s, rows, False), om.token_mask(f, s, False)[rows])
+
+
+@pytest.mark.parametrize("sink", [False, True])
+def test_kept_tiles_of_selected_query_tiles(sink):
+    # the sweep restricted to some query tiles gives those rows of the map
+    for f, s, T in [(4, 9, 4), (8, 16, 8), (5, 7, 3), (33, 3, 16), (9, 100, 64), (40, 20, 64)]:
+        full = om.kept_tiles(f, s, T, sink)
+        nb = full.shape[0]
+        for tiles in ([0], [nb - 1], list(range(0, nb, 3)), [nb - 1, 0, nb // 2]):
+            assert np.array_equal(om.kept_tiles(f, s, T, sink, tiles=tiles), full[tiles]), (f, s, T)
+        v = om.Variant(decay="harmonic", central=2)
+        assert np.array_equal(om.kept_tiles(f, s, T, sink, v, tiles=[nb - 1, 1]),
+                              om.kept_tiles(f, s, T, sink, v)[[nb - 1, 1]])
