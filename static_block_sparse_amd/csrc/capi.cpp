@@ -61,9 +61,11 @@ int check_common(const radial_layout *L, int32_t B, int32_t H, int64_t N, int32_
   if (B < 1 || H < 1) return fail(RADIAL_E_INVALID, "B and H must be >= 1");
   // one (batch, head) slice must stay below 2^31 bytes: the kernels address
   // rows within a slice with 32-bit offsets
-  if (N < 1 || (D > 0 && N > ((int64_t(1) << 31) - 1) / (2 * (int64_t)D)))
-    return fail(RADIAL_E_UNSUPPORTED, "N * D * 2 = " + std::to_string(N * 2 * (int64_t)D) +
-                                          " bytes per (batch, head); must be < 2^31");
+  if (N < 1) return fail(RADIAL_E_INVALID, "N must be >= 1");
+  if (D > 0 && N > ((int64_t(1) << 31) - 1) / (2 * (int64_t)D))
+    return fail(RADIAL_E_UNSUPPORTED, "N = " + std::to_string(N) + " at D = " + std::to_string(D) +
+                                          ": one (batch, head) slice of N * D bf16 values must "
+                                          "hold fewer than 2^31 bytes");
   if (N != L->n)
     return fail(RADIAL_E_SHAPE, "N = " + std::to_string(N) + " but the layout has n = " +
                                     std::to_string(L->n) + " (frames * tokens_per_frame)");

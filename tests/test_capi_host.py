@@ -274,6 +274,9 @@ def test_compute_calls_reject_slices_of_2_gib_or_more():
         assert "2^31" in lib.radial_last_error().decode()
         ba = (L.handle, 1, 1, N, D, 0.125) + (dummy,) * 10 + (1 << 20, None)
         assert lib.radial_attn_bwd(*ba) == -2, (N, D)
+    for N in (0, -5):
+        fa = (L.handle, 1, 1, N, 64, 0.125, dummy, dummy, dummy, dummy, dummy, None)
+        assert lib.radial_attn_fwd(*fa) == -1
     # the largest N below the limit only fails the layout comparison
     N = (1 << 31) // 256 - 1
     fa = (L.handle, 1, 1, N, 128, 0.125, dummy, dummy, dummy, dummy, dummy, None)
