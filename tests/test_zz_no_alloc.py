@@ -85,3 +85,37 @@ def test_noalloc_backward_refuses_sizes_beyond_the_scratch():
     assert st == -2, st
     assert "scratch" in sba.lib().radial_last_error().decode()
     torch.cuda.synchronize()
+
+
+def test_noalloc_backward_under_graph_capture():
+    # the callers the entry point is for: the forward and the allocation-free
+    # backward captured in one graph (layout uploaded and outputs allocated
+    # beforehand), replayed three times with eager work and a synchronisation
+    # between replays; every replay must give the eager result bit for bit
+    f, s, T, D, B, H = 6, 300, 128, 128, 1, 2
+    L = sba.Layout(f, s, T).upload()
+    q, k, v, do = (t.cuda() for t in workloads.make_inputs(B, H, f * s, D, 77, with_dout=True))
+    o_ref, lse_ref = sba.attn_fwd(q, k, v, L)
+    ref = sba.attn_bwd(q, k, v, o_ref, lse_ref, do, L)
+    o, lse = torch.empty_like(q), torch.empty_like(lse_ref)
+    grads = tuple(torch.empty_like(q) for _ in range(3))
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm-up on the capture stream
+        sba.attn_fwd(q, k, v, L, out=o, lse=lse)
+        sba.attn_bwd_noalloc(q, k, v, o, lse, do, L, out=grads)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        sba.attn_fwd(q, k, v, L, out=o, lse=lse)
+        sba.attn_bwd_noalloc(q, k, v, o, lse, do, L, out=grads)
+    for rep in range(3):
+        for t in (o, lse) + grads:
+            t.fill_(float("nan"))  # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_ref) and torch.equal(lse, lse_ref), rep
+        for name, a, b in zip(("dq", "dk", "dv"), grads, ref):
+            assert torch.equal(a, b), (rep, name)
