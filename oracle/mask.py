@@ -20,7 +20,10 @@ with its reason in the design notes):
   pairs whose distance is a multiple of ceil(2**r / s), so the amortised
   density of that band is about 1/2**r, the same decay as the bands above it
   (review Step 2-C; paper Fig.5 caption, Eq.4; rebuttal "Whether to Reduce
-  the Diagonal Frequency when the Width is below 1").
+  the Diagonal Frequency when the Width is below 1").  The pages print no
+  numbers for this rule: the tests pin the structure (empty or diagonal
+  blocks) and the band density within (2^-r / 2, 2^-r] read off the mask,
+  but the exact period inside that bound is parity unpinned.
 * attention sink: every query may attend every key of frame 0 (review Step 4;
   paper §4.2, Appx A.1 Eq.8).  Column sink only.
 * tile semantics: a T x T tile of the n x n mask is kept when at least one
