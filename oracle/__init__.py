@@ -28,9 +28,14 @@ Modules:
 Parity status: every function is pinned by a ``-m "not gpu"`` test in
 ``tests/test_oracle_*.py`` against the review's worked example, closed forms,
 brute force or a library routine (torch SDPA / autograd in float64).  The
-sub-1-width sampling rule (``band`` with w == 0) is pinned only by the
-power-of-two special case s == 1 and the amortised-density identity; the
-pages give no worked numbers for it.
+sub-1-width sampling rule (``band`` with w == 0) is pinned by the
+power-of-two special case s == 1 and, read off the brute-force mask at
+frame sizes where ceil and floor of 2^r / s differ, by its structure (empty
+or diagonal blocks) and the band density bound (2^-r / 2, 2^-r]; the pages
+give no worked numbers for it, so the exact period inside that bound is
+parity unpinned.  ``attention.bwd_dkdv_tile`` / ``row_stats`` (per key tile)
+and ``fwd_rows`` / ``dq_rows`` (per query row set) are pinned against the
+whole-head functions and torch float64 autograd.
 """
 
 from . import mask, attention  # noqa: F401
