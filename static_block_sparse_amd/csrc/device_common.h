@@ -163,42 +163,44 @@ __device__ __forceinline__ u32x4 rsrc_words(const void *p, int bytes) {
   return r;
 }
 
+// LDS offset of a generic pointer into LDS: the low 32 bits of a flat
+// address inside the LDS aperture (the aperture base has zero low bits).
+// Unlike an address-space cast this needs no null check; p must point into
+// LDS.
+__device__ __forceinline__ unsigned lds_offset(const void *p) {
+  return (unsigned)(unsigned long long)p;
+}
+
 // dma16 issued from inline assembly.  The compiler does not see this copy,
 // so it adds no vmcnt waits of its own before LDS reads that it cannot prove
 // disjoint from the copy's destination (it cannot for the transposing reads,
 // and would otherwise make every copy complete before the next V^T read).
 // The caller therefore owns the wait: s_waitcnt vmcnt(0) (wait_vmem) and a
 // barrier before anyone reads the destination.  The instruction writes LDS
-// only (no register results), and M0, which carries the LDS address, is
-// restored afterwards.
+// only (no register results).  M0 carries the LDS address; it is declared
+// clobbered, so the compiler sets it again wherever it needs it.
 __device__ __forceinline__ void dma16_async(u32x4 r, const bf16 *lds_block, int byte_off) {
-  const unsigned lds_addr = __builtin_amdgcn_readfirstlane(
-      (unsigned)(unsigned long)(__attribute__((address_space(3))) const void *)lds_block);
-  unsigned saved;
+  const unsigned lds_addr = __builtin_amdgcn_readfirstlane(lds_offset(lds_block));
   asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %1\n\t"
+      "s_mov_b32 m0, %0\n\t"
       "s_nop 0\n\t"
-      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "s"(lds_addr), "v"(byte_off), "s"(r));
+      "buffer_load_dwordx4 %1, %2, 0 offen lds"
+      :
+      : "s"(lds_addr), "v"(byte_off), "s"(r)
+      : "m0");
 }
 
 // The 4-byte form of dma16_async: lane l writes LDS bytes [4 l, 4 l + 4) of
 // lds_block from byte offset byte_off of the resource.
 __device__ __forceinline__ void dma4_async(u32x4 r, const void *lds_block, int byte_off) {
-  const unsigned lds_addr = __builtin_amdgcn_readfirstlane(
-      (unsigned)(unsigned long)(__attribute__((address_space(3))) const void *)lds_block);
-  unsigned saved;
+  const unsigned lds_addr = __builtin_amdgcn_readfirstlane(lds_offset(lds_block));
   asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %1\n\t"
+      "s_mov_b32 m0, %0\n\t"
       "s_nop 0\n\t"
-      "buffer_load_dword %2, %3, 0 offen lds\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "s"(lds_addr), "v"(byte_off), "s"(r));
+      "buffer_load_dword %1, %2, 0 offen lds"
+      :
+      : "s"(lds_addr), "v"(byte_off), "s"(r)
+      : "m0");
 }
 
 // Copies a ROWS x D bf16 tile (row-major at `src`, `valid` rows before the
