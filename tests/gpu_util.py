@@ -24,6 +24,16 @@ value is off by at most 2^-8 of itself (on average about 2^-10 of it).
   in rms alone, so each element may also be off by
   ELEM_REL * |ref| = 2 u |ref| = 2^-7 |ref|: exactly the sum of those two
   worst cases, with no further margin.
+* Sums of many large terms: an element that sums n rounded terms t_i (O over
+  keys, dK / dV over queries) carries the random-signed rounding of every
+  term, an error with standard deviation u / sqrt(3) * sqrt(sum t_i^2): it
+  scales with the terms, not with the element, whose value may cancel.
+  Where few keys share each softmax row (large P) and one key is attended by
+  every query (the sink of a mask with one or two tokens per frame), that
+  error exceeds both the element-wise allowance and the rms guard.  Tests of
+  such masks pass the per-element term scales sqrt(sum t_i^2) (``term_scales``)
+  and each element may then be off by TERM_K times its scale, 4 standard
+  deviations, instead of ELEM_REL |ref| when that is larger.
 * LSE: fp32 log-sum-exp of fp32 logits: max |dLSE| <= 1e-3.
 * Gradients: dQ, dK, dV are rounded to bf16 and built from bf16-rounded P
   and dS, the same error structure as O, so the same relative guards apply
@@ -54,6 +64,7 @@ O_MEAN_ABS = 2e-3
 REL_MAX = 5e-2
 REL_MEAN = 1e-2
 ELEM_REL = 2 * 2.0 ** -8
+TERM_K = 4 * 2.0 ** -8 / np.sqrt(3)
 LSE_MAX_ABS = 1e-3
 PEAKY_REL_MAX = 1e-1
 
@@ -63,15 +74,21 @@ def f64(t: torch.Tensor) -> np.ndarray:
 
 
 def check_close(got: np.ndarray, ref: np.ndarray, what: str, absolute: bool = True,
-                normalise: bool = False, rel_max: float = REL_MAX, rel_mean: float = REL_MEAN):
-    """Assert the forward/gradient tolerances above; returns the error stats."""
+                normalise: bool = False, rel_max: float = REL_MAX, rel_mean: float = REL_MEAN,
+                term=None):
+    """Assert the forward/gradient tolerances above; returns the error stats.
+    ``term``: optional per-element term scales (see ``term_scales``)."""
     assert got.shape == ref.shape, (what, got.shape, ref.shape)
     assert np.isfinite(got).all(), f"{what}: non-finite values"
     err = np.abs(got - ref)
     rms = float(np.sqrt(np.mean(ref ** 2)))
     stats = dict(max_abs=float(err.max()), mean_abs=float(err.mean()), rms_ref=rms)
     norm = max(1.0, rms) if normalise else 1.0
-    excess = float((err - ELEM_REL * np.abs(ref)).max())
+    allow = ELEM_REL * np.abs(ref)
+    if term is not None:
+        assert term.shape == ref.shape, (what, term.shape)
+        allow = np.maximum(allow, TERM_K * term)
+    excess = float((err - allow).max())
     stats["max_excess"] = excess
     if absolute:
         # O: the stated max-abs target as is; gradients (normalise=True):
@@ -83,6 +100,22 @@ def check_close(got: np.ndarray, ref: np.ndarray, what: str, absolute: bool = Tr
         assert excess <= rel_max * rms, (what, stats)
         assert stats["mean_abs"] <= rel_mean * rms, (what, stats)
     return stats
+
+
+def term_scales(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray, mask: np.ndarray,
+                scale: float) -> dict:
+    """Per-element sqrt(sum of squared terms) of O, dQ, dK and dV for one
+    (batch, head) under a boolean token mask (float64 [n, D] inputs): the
+    scale of the rounding error of each element's sum (see above).  The
+    terms are those of the textbook forms, P V for O, scale dS K for dQ,
+    scale dS^T Q for dK and P^T dO for dV."""
+    z = np.where(mask, scale * (q @ k.T), -np.inf)
+    p = np.exp(z - z.max(axis=1, keepdims=True))
+    p /= p.sum(axis=1, keepdims=True)
+    ds = p * (do @ v.T - (do * (p @ v)).sum(axis=1, keepdims=True))
+    p2, ds2 = p ** 2, ds ** 2
+    return dict(o=np.sqrt(p2 @ v ** 2), dq=scale * np.sqrt(ds2 @ k ** 2),
+                dk=scale * np.sqrt(ds2.T @ q ** 2), dv=np.sqrt(p2.T @ do ** 2))
 
 
 def check_lse(got: np.ndarray, ref: np.ndarray, what: str = "lse"):
