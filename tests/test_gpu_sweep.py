@@ -13,7 +13,7 @@ sampled diagonals below unit width and layouts that are dense, and masks
 with one or two tokens per frame, where every query attends the sink keys
 and each softmax row holds only a few keys: the gradients of those keys sum
 thousands of large rounded terms, so every element gets the term-scaled
-allowance (``gpu_util.term_scales``).
+allowance (``gpu_util.rounding_sigmas``).
 """
 
 import sys
@@ -24,7 +24,7 @@ import torch
 
 import static_block_sparse_amd as sba
 import workloads
-from gpu_util import check_close, check_lse, f64, term_scales
+from gpu_util import check_close, check_lse, f64, rounding_sigmas
 from oracle import attention as oa
 from oracle import mask as om
 
@@ -32,7 +32,7 @@ pytestmark = pytest.mark.gpu
 
 V = om.Variant
 PAIRS = [(64, 64), (64, 128), (128, 128)]  # (head dim, tile)
-N_CASES = 40
+N_CASES = 120
 
 
 def _cases():
@@ -91,7 +91,7 @@ def test_random_configuration(case):
             else:
                 ro, rl = oa.fwd(*args, kept, T, scale)
                 rq, rk, rv = oa.bwd(*args, f64(do[b, h]), kept, T, scale)
-            ts = term_scales(*args, f64(do[b, h]), mask, scale)
+            ts = rounding_sigmas(*args, f64(do[b, h]), mask, scale)
             tag = f"case {case} b={b} h={h}"
             check_close(f64(o[b, h]), ro, f"O {tag}", term=ts["o"])
             check_lse(f64(lse[b, h]), rl, f"LSE {tag}")
