@@ -127,6 +127,18 @@ def bwd_masked(q, k, v, do, mask, scale):
     return scale * (ds @ k), scale * (ds.T @ q), p.T @ do
 
 
+def dq_masked(q_rows: np.ndarray, k: np.ndarray, v: np.ndarray, do_rows: np.ndarray,
+              mask_rows: np.ndarray, scale: float) -> np.ndarray:
+    """dQ of some query rows under their rows of a boolean token mask
+    [r, n]: the first gradient of ``bwd_masked`` for those rows alone (a
+    query row's gradient depends only on its own softmax row)."""
+    z = np.where(mask_rows, scale * (q_rows @ k.T), -np.inf)
+    p, _ = _softmax_rows(z)
+    dp = do_rows @ v.T
+    delta = (p * dp).sum(axis=1, keepdims=True)
+    return scale * ((p * (dp - delta)) @ k)
+
+
 def dq_rows(q_rows: np.ndarray, k_cols: np.ndarray, v_cols: np.ndarray,
             do_rows: np.ndarray, scale: float) -> np.ndarray:
     """dQ of some query rows over the keys they may attend (as ``fwd_rows``):

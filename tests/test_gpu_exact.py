@@ -4,7 +4,8 @@ With ``Layout(..., token_exact=True)`` the kernels apply the token predicate
 inside the kept tiles the mask only partly covers, so forward and backward
 must equal plain attention under the token mask (oracle ``fwd_masked`` /
 ``bwd_masked`` with ``token_mask``).  Small shapes are compared element by
-element over every head; the full-size 720p workload on sampled query rows
+element over every head; the full-size 720p workload and the 129-frame one
+(where more than half of the kept tiles are partial) on sampled query rows
 (forward O/LSE and dQ) and through the gradient identities.
 """
 
@@ -104,11 +105,12 @@ def test_all_full_tiles_match_tile_mode():
         assert torch.equal(x, y)
 
 
-def test_exact_full_size_sampled_rows():
-    """720p, 33 frames x 3600 tokens, 24 heads in one launch: O, LSE and dQ
-    on sampled query tiles of the first and last heads against the token
-    oracle; dK and dV through identities that hold at any size."""
-    w = workloads.WORKLOADS["hunyuan_5s_720p"]
+@pytest.mark.parametrize("name", ["hunyuan_5s_720p", "hunyuan_4x_long"])
+def test_exact_full_size_sampled_rows(name):
+    """720p (33 frames) and 129 frames of 3600 tokens, 24 heads in one launch:
+    O, LSE and dQ on sampled query tiles of the first and last heads against
+    the token oracle; dK and dV through identities that hold at any size."""
+    w = workloads.WORKLOADS[name]
     _say(f"[exact-full] B={w.B} H={w.H} N={w.N} D={w.D}")
     q, k, v, do = workloads.workload_inputs(w, with_dout=True, device="cuda")
     L = sba.Layout(w.frames, w.tokens_per_frame, w.T, token_exact=True)
@@ -127,7 +129,7 @@ def test_exact_full_size_sampled_rows():
             check_close(f64(o[0, h, rows]), ro, f"O h={h} tile={u}")
             check_lse(f64(lse[0, h, rows]), rl, f"lse h={h} tile={u}")
             # a query row's dQ depends only on its own softmax row
-            rq = oa.bwd_masked(qh[rows], kh, vh, dh[rows], m, w.scale)[0]
+            rq = oa.dq_masked(qh[rows], kh, vh, dh[rows], m, w.scale)
             check_close(f64(dq[0, h, rows]), rq, f"dQ h={h} tile={u}", normalise=True)
     # every softmax row sums to one: sum_n dV[n] = sum_m dO[m]; each dS row
     # sums to zero: sum_n dK[n] = 0.  Each of N bf16-rounded terms is off by

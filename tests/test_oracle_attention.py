@@ -115,6 +115,10 @@ def test_backward_equals_autograd(f, s, T):
     g = oa.bwd_masked(q, k, v, do, m, scale)
     for a, b in zip(g, (tq2.grad, tk2.grad, tv2.grad)):
         np.testing.assert_allclose(a, b.numpy(), rtol=0, atol=1e-12)
+    # dQ of a subset of rows from their mask rows alone equals autograd's
+    rows = np.array([0, n // 3, n - 1])
+    np.testing.assert_allclose(oa.dq_masked(q[rows], k, v, do[rows], m[rows], scale),
+                               tq2.grad.numpy()[rows], rtol=0, atol=1e-12)
 
 
 def test_backward_finite_differences():
