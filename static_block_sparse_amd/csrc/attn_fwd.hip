@@ -26,9 +26,13 @@
 //    offset and keys past N read as zeros.  Chunks are double buffered: the
 //    copy of chunk c + 1 is issued before the products of chunk c, with one
 //    barrier per chunk.
-//  * the running max is only moved when a chunk's max exceeds it by more
-//    than 8 (log2 units); probabilities then stay below 2^8, exact in the
-//    final O / l and LSE, and the O rescale is skipped on most chunks.
+//  * the running max is a reference value that moves lazily: a chunk's
+//    probabilities are formed against it directly, and only when one of a
+//    lane's exceeds 2^16 (seen from the lane's chunk sum, which bounds them
+//    all) is the chunk redone with its true row max, moving the reference
+//    when that exceeds it by more than 8 (log2 units).  The ratios O / l
+//    and the LSE are exact whatever the reference; the max reduction and
+//    the O rescale are skipped on almost every chunk.
 //  * query-tile groups: a workgroup of G T / 32 waves takes G query tiles
 //    (G = 3, three waves per SIMD; pairs or single tiles only when the mask
 //    compiler built no triple lists) and walks the sorted union of their key
@@ -98,6 +102,7 @@ radial_fwd_kernel(const bf16 *__restrict__ Q, const bf16 *__restrict__ K,
   using C = FwdCfg<D, T, G>;
   using GB = GroupBits<G>;
   constexpr float kSlack = 8.f;  // lazy-rescale threshold (log2 units)
+  constexpr float kBound = 65536.f;  // probabilities accepted without a new max
   __shared__ __attribute__((aligned(1024))) bf16 lds[2 * C::BUF];
 
   const int tid = threadIdx.x;
@@ -241,72 +246,89 @@ radial_fwd_kernel(const bf16 *__restrict__ Q, const bf16 *__restrict__ K,
       // S^T for the wave's 32 queries against the chunk's KC keys, the K
       // fragments read four products ahead (products in the order kk, kb);
       // two in token-exact mode, whose predicate needs registers of its own
-      // (with four, triples spill inside the chunk loop there)
+      // (with four, triples spill inside the chunk loop there).  Keys at or
+      // past N and, in token-exact mode, keys outside the query's runs get
+      // -inf.
       f32x16 s[C::NKB];
-      bf16x8 kf[C::NKB][C::NKK];
+      auto scores = [&]() __attribute__((always_inline)) {
+        bf16x8 kf[C::NKB][C::NKK];
 #pragma unroll
-      for (int kk = 0; kk < C::NKK; ++kk)
+        for (int kk = 0; kk < C::NKK; ++kk)
+#pragma unroll
+          for (int kb = 0; kb < C::NKB; ++kb)
+            kf[kb][kk] = ld8(Ks + kb * 32 * D + kof[kk]);
+#pragma unroll
+        for (int kb = 0; kb < C::NKB; ++kb) s[kb] = zero16();
+#pragma unroll
+        for (int kk = 0; kk < C::NKK; ++kk)
+#pragma unroll
+          for (int kb = 0; kb < C::NKB; ++kb) s[kb] = mfma32(kf[kb][kk], qf[kk], s[kb]);
+        read_ahead_order<1, EXACT ? 2 : 4, C::NKK * C::NKB, 1>();
+        // the tail chunk: keys at or past N, which sit at offsets from
+        // key0 + 4 g of N - key0 - 4 g and beyond
+        if (key0 + C::KC > N) mask_elems(s, rank_mask<C::NKB>(N - key0 - 4 * g));
+        if (partial) {
+          const unsigned lid =
+              __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+          const int qr = qrow0 + (int)(lid & 31u);  // this lane's query row
+          const int qi = bctx.div_s(qr), qa = qr - qi * bctx.s;
+          const unsigned ok = lane_key_bits<C::NKB>(bctx, qi, qa, key0, g);
+          if (__ballot(ok != ~0u)) mask_elems(s, ok);  // some key of the wave's block is masked
+        }
+      };
+      // P = 2^(scale_log2 S - m_run) rounded to bf16, and this lane's sum
+      bf16x8 pf[C::NKB][2];
+      float lc;
+      auto probs = [&]() __attribute__((always_inline)) {
+        float psum[4] = {0.f, 0.f, 0.f, 0.f};  // four partial sums: short add chains
+#pragma unroll
+        for (int kb = 0; kb < C::NKB; ++kb) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float p = fast_exp2(fmaf(s[kb][r], scale_log2, -m_run));
+            psum[r & 3] += p;
+            pf[kb][r >> 3][r & 7] = bf16(p);
+          }
+        }
+        lc = (psum[0] + psum[1]) + (psum[2] + psum[3]);
+        // the bf16 P is formed here, not after the branch below: sunk past
+        // it, the fp32 probabilities stay live and the loop spills
 #pragma unroll
         for (int kb = 0; kb < C::NKB; ++kb)
-          kf[kb][kk] = ld8(Ks + kb * 32 * D + kof[kk]);
 #pragma unroll
-      for (int kb = 0; kb < C::NKB; ++kb) s[kb] = zero16();
-#pragma unroll
-      for (int kk = 0; kk < C::NKK; ++kk)
-#pragma unroll
-        for (int kb = 0; kb < C::NKB; ++kb) s[kb] = mfma32(kf[kb][kk], qf[kk], s[kb]);
-      read_ahead_order<1, EXACT ? 2 : 4, C::NKK * C::NKB, 1>();
-      if (key0 + C::KC > N) {  // the tail chunk: keys at or past N get -inf
-        // register r of block kb holds key key0 + kb*32 + 8*(r/4) + 4g + r%4
-        const int lim = N - key0 - 4 * g;
-#pragma unroll
-        for (int kb = 0; kb < C::NKB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (kb * 32 + 8 * (r >> 2) + (r & 3) >= lim) s[kb][r] = -INFINITY;
-      }
-      if (partial) {  // token-exact: keys outside the query's runs get -inf
-        const unsigned lid = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
-        const int qr = qrow0 + (int)(lid & 31u);  // this lane's query row
-        const int qi = bctx.div_s(qr), qa = qr - qi * bctx.s;
-        const unsigned ok = lane_key_bits<C::NKB>(bctx, qi, qa, key0, g);
-        if (__ballot(ok != ~0u)) {  // some key of the wave's block is masked
+          for (int h = 0; h < 2; ++h) asm volatile("" : "+v"(pf[kb][h]));
+      };
+      // The reference max is checked through the sum, not a max over the
+      // chunk: lc >= every probability of the lane, so lc <= kBound bounds
+      // them all (and fails on inf or NaN).  Only then, which is every
+      // wave's first chunk (m_run starts at kNoMax) and rarely after it,
+      // the chunk is redone: S again (the exponentials overwrote it), its
+      // row max, the lazy move of m_run and the rescale of O and l, after
+      // which every probability is at most 2^kSlack.
+      bool redo = false;
+      for (;;) {
+        scores();
+        if (redo) {
+          float mx = -INFINITY;
 #pragma unroll
           for (int kb = 0; kb < C::NKB; ++kb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-              if (!((ok >> (16 * kb + r)) & 1u)) s[kb][r] = -INFINITY;
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+          const float m_new = pair_max(mx) * scale_log2;
+          const bool mv = m_new > m_run + kSlack;
+          const float alpha = mv ? fast_exp2(m_run - m_new) : 1.f;
+          m_run = mv ? m_new : m_run;
+          l_run *= alpha;
+#pragma unroll
+          for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
         }
+        probs();
+        if (redo || !__ballot(!(lc <= kBound))) break;
+        redo = true;
       }
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < C::NKB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-      const float m_new = pair_max(mx) * scale_log2;
-      if (__ballot(m_new > m_run + kSlack)) {
-        const bool mv = m_new > m_run + kSlack;
-        const float alpha = mv ? fast_exp2(m_run - m_new) : 1.f;
-        m_run = mv ? m_new : m_run;
-        l_run *= alpha;
-#pragma unroll
-        for (int db = 0; db < C::NDB; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-      }
-
-      bf16x8 pf[C::NKB][2];
-      float psum[4] = {0.f, 0.f, 0.f, 0.f};  // four partial sums: short add chains
-#pragma unroll
-      for (int kb = 0; kb < C::NKB; ++kb) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = fast_exp2(fmaf(s[kb][r], scale_log2, -m_run));
-          psum[r & 3] += p;
-          pf[kb][r >> 3][r & 7] = bf16(p);
-        }
-      }
-      l_run += (psum[0] + psum[1]) + (psum[2] + psum[3]);
+      l_run += lc;
 
       // O^T += V^T P^T
 #pragma unroll

@@ -396,6 +396,25 @@ __device__ __forceinline__ unsigned lane_query_bits(const BandCtx &c, int kj, in
   return lane_pair_bits<1, true>(c, kj, kb, row0, g);
 }
 
+// s[kb][r] = -inf where bit 16 kb + r of ok is clear (register r of block kb
+// is the lane's element of that bit, see lane_pair_bits).  Each element
+// takes its bit sign-extended (all ones or zero) as a bit-select mask: two
+// vector instructions per element and no compare, so no condition register
+// per element (compare results held in scalar register pairs overflowed the
+// scalar register file where several masks meet).
+template <int NB>
+__device__ __forceinline__ void mask_elems(f32x16 (&s)[NB], unsigned ok) {
+  const float ninf = -INFINITY;
+#pragma unroll
+  for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      int m;
+      asm("v_bfe_i32 %0, %1, %2, 1" : "=v"(m) : "v"(ok), "i"(16 * kb + r));
+      asm("v_bfi_b32 %0, %1, %0, %2" : "+v"(s[kb][r]) : "v"(m), "v"(ninf));
+    }
+}
+
 // A running maximum that starts finite: a row whose first chunks are fully
 // masked (token-exact layouts) then exponentiates -inf - m = -inf to 0
 // instead of -inf + inf = NaN.
