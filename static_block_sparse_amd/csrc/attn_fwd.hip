@@ -227,6 +227,13 @@ radial_fwd_kernel(const bf16 *__restrict__ Q, const bf16 *__restrict__ K,
     }
   }
 
+  // The tail chunk (keys key0 .. key0 + KC - 1 with key0 + KC > N, the
+  // last chunk when KC does not divide N): its keys at or past N sit at
+  // offsets N - key0 - 4 g and beyond from the lane's base key0 + 4 g, so
+  // the mask words of the two lane halves are constants of the launch.
+  const int tail_y = N - (N - 1) / C::KC * C::KC;
+  const unsigned tail_ok0 = rank_mask<C::NKB>(tail_y), tail_ok1 = rank_mask<C::NKB>(tail_y - 4);
+
   // chunk c from buffer BS (0 or 1, = c % 2)
   auto chunk = [&](int c, auto BS) __attribute__((always_inline)) {
     constexpr int bsel = decltype(BS)::value;
@@ -264,9 +271,7 @@ radial_fwd_kernel(const bf16 *__restrict__ Q, const bf16 *__restrict__ K,
 #pragma unroll
           for (int kb = 0; kb < C::NKB; ++kb) s[kb] = mfma32(kf[kb][kk], qf[kk], s[kb]);
         read_ahead_order<1, EXACT ? 2 : 4, C::NKK * C::NKB, 1>();
-        // the tail chunk: keys at or past N, which sit at offsets from
-        // key0 + 4 g of N - key0 - 4 g and beyond
-        if (key0 + C::KC > N) mask_elems(s, rank_mask<C::NKB>(N - key0 - 4 * g));
+        if (key0 + C::KC > N) mask_elems(s, g ? tail_ok1 : tail_ok0);  // the tail chunk
         if (partial) {
           const unsigned lid =
               __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
@@ -305,6 +310,8 @@ radial_fwd_kernel(const bf16 *__restrict__ Q, const bf16 *__restrict__ K,
       // the chunk is redone: S again (the exponentials overwrote it), its
       // row max, the lazy move of m_run and the rescale of O and l, after
       // which every probability is at most 2^kSlack.
+      // (a bool: with the flag as an integer or a ballot mask the compiler
+      // peels the first pass, and the loop spills)
       bool redo = false;
       for (;;) {
         scores();
