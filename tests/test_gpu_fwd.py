@@ -91,6 +91,41 @@ def test_peaky_softmax():
     _run_full_compare(8, 256, 64, 64, 1, 2, seed=42, scale=8.0 / np.sqrt(64))
 
 
+@pytest.mark.parametrize("gain", [6.0, 40.0])
+@pytest.mark.parametrize("exact", [False, True])
+def test_reference_max_moves_late_in_the_walk(gain, exact):
+    # Keys of the last frame get `gain` times larger logits.  Rows of the
+    # last frames take their reference max from the sink tile, the first of
+    # their walk, and meet the large logits in its last chunks: at gain 6
+    # (logits up to ~25 in log2 units above the reference) the chunk sum
+    # exceeds the bound while finite, at gain 40 (~170 above) the
+    # probabilities overflow to inf.  Either way the chunk is redone with its
+    # true max, so O and LSE match the oracle.
+    f, s, T, D, H = 6, 300, 128, 128, 2
+    N = f * s
+    _say(f"[fwd-late-max] gain={gain} exact={exact}")
+    q, k, v = workloads.make_inputs(1, H, N, D, 61)
+    k = k.clone()
+    k[:, :, (f - 1) * s:] = (k[:, :, (f - 1) * s:].float() * gain).to(torch.bfloat16)
+    L = sba.Layout(f, s, T, token_exact=exact)
+    scale = 1.0 / np.sqrt(D)
+    o, lse = sba.attn_fwd(q.cuda(), k.cuda(), v.cuda(), L, scale)
+    torch.cuda.synchronize()
+    go, gl = f64(o), f64(lse)
+    kept = om.kept_tiles(f, s, T, True)
+    mask = om.token_mask(f, s, True) if exact else None
+    for h in range(H):
+        qh, kh, vh = f64(q[0, h]), f64(k[0, h]), f64(v[0, h])
+        if exact:
+            ro, rl = oa.fwd_masked(qh, kh, vh, mask, scale)
+        else:
+            ro, rl = oa.fwd(qh, kh, vh, kept, T, scale)
+        # the last frame's rows really are dominated by the large logits
+        assert float(rl[(f - 1) * s:].mean()) > 10.0
+        check_close(go[0, h], ro, f"O h={h}")
+        check_lse(gl[0, h], rl)
+
+
 def test_dense_layout_is_plain_attention():
     go, _ = _run_full_compare(4, 300, 128, 128, 1, 2, seed=51, dense=True)
     # and against torch's float64 SDPA on the CPU (a library routine)
