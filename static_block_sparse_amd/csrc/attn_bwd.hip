@@ -274,7 +274,7 @@ __global__ __launch_bounds__(T / 32 * 64, 1) void radial_bwd_dkdv_kernel(
   // (flag FP), so no step starts by waiting for LDS.  Those operands belong
   // to a chunk that landed at least one barrier earlier and whose buffer is
   // refilled two barriers later.
-  constexpr int RA = 4;                                 // read-ahead (slots)
+  constexpr int RA = 8;                                 // read-ahead (slots)
   auto step = [&](auto F1, auto F2, auto F3, auto FP, auto FN, int b1, int m1, int b2, int m2,
                   int b3, int m3, int b3n, int m3n, bf16x8 (&pre)[RA], Blk &sd_new,
                   const Blk &sd_old, bf16x8 (&pd_new)[2][2], const bf16x8 (&pd_old)[2][2],
