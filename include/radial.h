@@ -266,6 +266,13 @@ int radial_attn_bwd_noalloc(const radial_layout *L, int32_t B, int32_t H, int64_
    value outside 1..3.  Not for concurrent use with forward calls. */
 int radial_test_set_fwd_group(int32_t max_group);
 
+/* Test hook: while on = 1, radial_mask_build[_ex] and radial_layout_upload
+   fail with RADIAL_E_NOMEM before allocating anything (0 restores normal
+   behaviour), so tests can reach the allocation-failure paths.  Returns the
+   previous setting, or RADIAL_E_INVALID for a value other than 0 or 1.  Not
+   for concurrent use with layout calls. */
+int radial_test_set_fail_alloc(int32_t on);
+
 /* Static text for a status code. */
 const char *radial_status_string(int status);
 

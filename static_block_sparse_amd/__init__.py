@@ -70,6 +70,7 @@ def _declare(L):
         "radial_attn_bwd_noalloc": (c.c_int, [vp, i32, i32, i64, i32, f32, vp, vp, vp, vp, vp,
                                               vp, vp, vp, vp, vp]),
         "radial_test_set_fwd_group": (c.c_int, [i32]),
+        "radial_test_set_fail_alloc": (c.c_int, [i32]),
         "radial_status_string": (c.c_char_p, [c.c_int]),
         "radial_last_error": (c.c_char_p, []),
     }

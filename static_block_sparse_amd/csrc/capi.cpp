@@ -28,12 +28,10 @@ int fail(int status, const std::string &msg) {
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Allocation-failure hook for tests: RADIAL_TEST_FAIL_ALLOC=1 makes every
-// host/device allocation in the library report RADIAL_E_NOMEM.
-bool forced_alloc_failure() {
-  const char *e = std::getenv("RADIAL_TEST_FAIL_ALLOC");
-  return e && e[0] == '1';
-}
+// Allocation-failure flag for tests (radial_test_set_fail_alloc): while set,
+// the layout build and upload report RADIAL_E_NOMEM instead of allocating.
+std::atomic<int32_t> g_fail_alloc{0};
+bool forced_alloc_failure() { return g_fail_alloc.load(std::memory_order_relaxed) != 0; }
 
 // Largest query-tile group the forward uses (3: triples); lowered only by
 // radial_test_set_fwd_group, so tests can compare the three forms.
@@ -434,6 +432,11 @@ int radial_attn_bwd_noalloc(const radial_layout *L, int32_t B, int32_t H, int64_
                                   hipGetErrorString(e));
   return run_bwd(L, B, H, N, D, scale, q, k, v, o, lse, dout, dq, dk, dv, scratch, need,
                  hip_stream);
+}
+
+int radial_test_set_fail_alloc(int32_t on) {
+  if (on != 0 && on != 1) return fail(RADIAL_E_INVALID, "on must be 0 or 1");
+  return g_fail_alloc.exchange(on);
 }
 
 int radial_test_set_fwd_group(int32_t max_group) {

@@ -171,11 +171,12 @@ int main() {
   setenv("FAKE_DEVICE_NONE", "1", 1);
   EXPECT(radial_layout_upload(L) == RADIAL_E_HIP);
   unsetenv("FAKE_DEVICE_NONE");
-  setenv("RADIAL_TEST_FAIL_ALLOC", "1", 1);
+  EXPECT(radial_test_set_fail_alloc(1) == 0);
   EXPECT(radial_layout_upload(L) == RADIAL_E_NOMEM);
   radial_layout *L2 = nullptr;
   EXPECT(radial_mask_build(8, 256, 64, RADIAL_SINK, &L2) == RADIAL_E_NOMEM && L2 == nullptr);
-  unsetenv("RADIAL_TEST_FAIL_ALLOC");
+  EXPECT(radial_test_set_fail_alloc(0) == 1);
+  EXPECT(radial_test_set_fail_alloc(5) == RADIAL_E_INVALID);
   EXPECT(radial_layout_upload(L) == RADIAL_OK);
   // slices of 2^31 bytes or more are refused before any launch (no buffer
   // of that size exists here: a launch would touch the small blocks below

@@ -328,14 +328,18 @@ def test_binding_rejects_host_tensors_before_any_launch():
         sba.attn_bwd(x, x, x, x, FakeLse(), x, L, workspace=ws_cpu)
 
 
-def test_allocation_failure_hook(monkeypatch):
-    monkeypatch.setenv("RADIAL_TEST_FAIL_ALLOC", "1")
+def test_allocation_failure_hook():
+    lib = sba.lib()
+    assert lib.radial_test_set_fail_alloc(2) == -1
     h = ctypes.c_void_p()
-    assert sba.lib().radial_mask_build(8, 256, 64, 1, ctypes.byref(h)) == -4
-    assert h.value is None
-    monkeypatch.setenv("RADIAL_TEST_FAIL_ALLOC", "0")
-    assert sba.lib().radial_mask_build(8, 256, 64, 1, ctypes.byref(h)) == 0
-    sba.lib().radial_layout_destroy(h)
+    assert lib.radial_test_set_fail_alloc(1) == 0
+    try:
+        assert lib.radial_mask_build(8, 256, 64, 1, ctypes.byref(h)) == -4
+        assert h.value is None
+    finally:
+        assert lib.radial_test_set_fail_alloc(0) == 1
+    assert lib.radial_mask_build(8, 256, 64, 1, ctypes.byref(h)) == 0
+    lib.radial_layout_destroy(h)
 
 
 def test_layout_is_o_n_log_n_at_tile_level_for_long_videos():

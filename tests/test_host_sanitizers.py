@@ -44,7 +44,6 @@ def driver():
 
 def test_host_code_is_clean_under_asan_and_ubsan(driver):
     env = dict(os.environ)
-    env.pop("RADIAL_TEST_FAIL_ALLOC", None)
     env["ASAN_OPTIONS"] = "detect_leaks=1:abort_on_error=0"
     env["UBSAN_OPTIONS"] = "print_stacktrace=1:halt_on_error=1"
     r = subprocess.run([driver], capture_output=True, text=True, env=env, timeout=600)
