@@ -253,11 +253,13 @@ radial_fwd_kernel(const bf16 *__restrict__ Q, const bf16 *__restrict__ K,
       // S^T for the wave's 32 queries against the chunk's KC keys, the K
       // fragments read four products ahead (products in the order kk, kb);
       // two in token-exact mode, whose predicate needs registers of its own
-      // (with four, triples spill inside the chunk loop there).  Keys at or
-      // past N and, in token-exact mode, keys outside the query's runs get
-      // -inf.
+      // (with four, triples spill inside the chunk loop there).  Keys outside
+      // the query's runs get -inf in token-exact mode, and with MT keys at or
+      // past N too (the tail chunk, see below).
       f32x16 s[C::NKB];
-      auto scores = [&]() __attribute__((always_inline)) {
+      const bool tail = key0 + C::KC > N;
+      auto scores = [&](auto MT) __attribute__((always_inline)) {
+        constexpr bool mask_tail = decltype(MT)::value;
         bf16x8 kf[C::NKB][C::NKK];
 #pragma unroll
         for (int kk = 0; kk < C::NKK; ++kk)
@@ -271,7 +273,9 @@ radial_fwd_kernel(const bf16 *__restrict__ Q, const bf16 *__restrict__ K,
 #pragma unroll
           for (int kb = 0; kb < C::NKB; ++kb) s[kb] = mfma32(kf[kb][kk], qf[kk], s[kb]);
         read_ahead_order<1, EXACT ? 2 : 4, C::NKK * C::NKB, 1>();
-        if (key0 + C::KC > N) mask_elems(s, g ? tail_ok1 : tail_ok0);  // the tail chunk
+        if constexpr (mask_tail) {
+          if (tail) mask_elems(s, g ? tail_ok1 : tail_ok0);  // the tail chunk
+        }
         if (partial) {
           const unsigned lid =
               __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
@@ -305,35 +309,34 @@ radial_fwd_kernel(const bf16 *__restrict__ Q, const bf16 *__restrict__ K,
       };
       // The reference max is checked through the sum, not a max over the
       // chunk: lc >= every probability of the lane, so lc <= kBound bounds
-      // them all (and fails on inf or NaN).  Only then, which is every
-      // wave's first chunk (m_run starts at kNoMax) and rarely after it,
-      // the chunk is redone: S again (the exponentials overwrote it), its
-      // row max, the lazy move of m_run and the rescale of O and l, after
-      // which every probability is at most 2^kSlack.
-      // (a bool: with the flag as an integer or a ballot mask the compiler
-      // peels the first pass, and the loop spills)
-      bool redo = false;
-      for (;;) {
-        scores();
-        if (redo) {
-          float mx = -INFINITY;
+      // them all (and fails on inf or NaN).  Only when that fails, which is
+      // every wave's first chunk (m_run starts at kNoMax) and rarely after
+      // it, or in the tail chunk, the chunk is redone: S again (the
+      // exponentials overwrote it), its row max, the lazy move of m_run and
+      // the rescale of O and l, after which every probability is at most
+      // 2^kSlack.  The first pass leaves the tail chunk's keys past N
+      // unmasked (the redo discards its probabilities), so the common pass
+      // has no branch between the products and the exponentials, and the
+      // compiler schedules the two together.
+      scores(FwdBuf<0>{});
+      probs();
+      if (__ballot(tail || !(lc <= kBound))) {
+        scores(FwdBuf<1>{});
+        float mx = -INFINITY;
 #pragma unroll
-          for (int kb = 0; kb < C::NKB; ++kb)
+        for (int kb = 0; kb < C::NKB; ++kb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-          const float m_new = pair_max(mx) * scale_log2;
-          const bool mv = m_new > m_run + kSlack;
-          const float alpha = mv ? fast_exp2(m_run - m_new) : 1.f;
-          m_run = mv ? m_new : m_run;
-          l_run *= alpha;
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+        const float m_new = pair_max(mx) * scale_log2;
+        const bool mv = m_new > m_run + kSlack;
+        const float alpha = mv ? fast_exp2(m_run - m_new) : 1.f;
+        m_run = mv ? m_new : m_run;
+        l_run *= alpha;
 #pragma unroll
-          for (int db = 0; db < C::NDB; ++db)
+        for (int db = 0; db < C::NDB; ++db)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-        }
+          for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
         probs();
-        if (redo || !__ballot(!(lc <= kBound))) break;
-        redo = true;
       }
       l_run += lc;
 
