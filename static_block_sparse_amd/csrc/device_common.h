@@ -177,8 +177,13 @@ __device__ __forceinline__ unsigned lds_offset(const void *p) {
 // and would otherwise make every copy complete before the next V^T read).
 // The caller therefore owns the wait: s_waitcnt vmcnt(0) (wait_vmem) and a
 // barrier before anyone reads the destination.  The instruction writes LDS
-// only (no register results).  M0 carries the LDS address; it is declared
-// clobbered, so the compiler sets it again wherever it needs it.
+// only (no register results).  M0 carries the LDS address.  M0 is a register
+// the compiler reserves, so listing it as clobbered does not oblige the
+// compiler to preserve it (it warns about exactly that): a kernel that uses
+// these copies must not have compiler-generated code that relies on M0.
+// The backward kernels have none (they use no compiler-issued copy to LDS);
+// a CPU test checks their compiled code for any M0 access outside these
+// statements.
 __device__ __forceinline__ void dma16_async(u32x4 r, const bf16 *lds_block, int byte_off) {
   const unsigned lds_addr = __builtin_amdgcn_readfirstlane(lds_offset(lds_block));
   asm volatile(

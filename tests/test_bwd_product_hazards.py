@@ -13,7 +13,9 @@ This test reads the compiled code, follows its branches, and checks that on
 every path at least four other matrix products issue between an
 inline-assembly product and the first other instruction that reads or writes
 its result registers.  A compiler or source change that moves such an access
-closer fails here, on the CPU, before it can reach a GPU.
+closer fails here, on the CPU, before it can reach a GPU.  It also checks
+that no compiler-generated instruction of the backward kernels touches M0,
+which the inline-assembly copies set without the compiler preserving it.
 """
 
 import heapq
@@ -103,7 +105,8 @@ def _fewest_products_before_access(ins, labels, i):
 
 
 @pytest.fixture(scope="module")
-def dkdv_assembly(tmp_path_factory):
+def bwd_assembly(tmp_path_factory):
+    """attn_bwd.hip compiled for gfx950 as the build compiles it, as text."""
     if not shutil.which(B.HIPCC) and not os.path.exists(B.HIPCC):
         pytest.skip("hipcc not available")
     out = tmp_path_factory.mktemp("asm") / "attn_bwd.s"
@@ -111,8 +114,12 @@ def dkdv_assembly(tmp_path_factory):
            "--cuda-device-only", "-S", os.path.join(B.CSRC, "attn_bwd.hip"), "-o", str(out)]
     r = subprocess.run(cmd, capture_output=True, text=True, timeout=600)
     assert r.returncode == 0, r.stderr[-4000:]
-    text = out.read_text()
-    funcs = re.findall(rf"^({KERNEL}):[^\n]*\n(.*?)^\.Lfunc_end", text, re.M | re.S)
+    return out.read_text()
+
+
+@pytest.fixture(scope="module")
+def dkdv_assembly(bwd_assembly):
+    funcs = re.findall(rf"^({KERNEL}):[^\n]*\n(.*?)^\.Lfunc_end", bwd_assembly, re.M | re.S)
     # every (D, T, token-exact) instantiation: (64, 64), (64, 128), (128, 128) x 2
     assert len(funcs) == 6, [f[0] for f in funcs]
     return funcs
@@ -172,3 +179,33 @@ def test_checker_flags_a_close_reader():
 """
     ins, labels = _parse(body_branch)
     assert _fewest_products_before_access(ins, labels, 0) == 0
+
+
+@pytest.fixture(scope="module")
+def bwd_functions(bwd_assembly):
+    funcs = re.findall(r"^(_ZN6radial\w+kernel\w+):[^\n]*\n(.*?)^\.Lfunc_end", bwd_assembly,
+                       re.M | re.S)
+    assert len(funcs) >= 20, len(funcs)
+    return funcs
+
+
+def test_m0_is_used_only_by_the_inline_assembly_copies(bwd_functions):
+    # The copies issued from inline assembly set M0 and list it as clobbered;
+    # M0 is reserved by the compiler, which does not promise to preserve it
+    # across them.  So no compiler-generated instruction of these kernels may
+    # touch M0 at all.
+    for name, body in bwd_functions:
+        in_asm, bad = False, []
+        for line in body.splitlines():
+            s = line.strip()
+            if s.startswith(";;#ASMSTART"):
+                in_asm = True
+                continue
+            if s.startswith(";;#ASMEND"):
+                in_asm = False
+                continue
+            if not s or s.startswith((";", ".")):
+                continue
+            if not in_asm and re.search(r"\bm0\b", s.split(";")[0]):
+                bad.append(s)
+        assert not bad, (name, bad[:4])
