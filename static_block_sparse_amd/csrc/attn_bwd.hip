@@ -119,6 +119,17 @@ struct BwdFlag {
   static constexpr int value = V;
 };
 
+// v = -inf unless bit `bit` (a constant after unrolling) of ok is set: the
+// bit sign-extended is a bit-select mask, two vector instructions and no
+// compare (a compare and select per element cost three, in every chunk of a
+// token-exact dK/dV walk, full tiles included)
+__device__ __forceinline__ float mask_bit(float v, unsigned ok, int bit) {
+  int m;
+  asm("v_bfe_i32 %0, %1, %2, 1" : "=v"(m) : "v"(ok), "i"(bit));
+  asm("v_bfi_b32 %0, %1, %0, %2" : "+v"(v) : "v"(m), "v"(-INFINITY));
+  return v;
+}
+
 template <int D, int T, bool EXACT>
 __global__ __launch_bounds__(T / 32 * 64, 1) void radial_bwd_dkdv_kernel(
     const bf16 *__restrict__ Q, const bf16 *__restrict__ K, const bf16 *__restrict__ V,
@@ -345,7 +356,7 @@ __global__ __launch_bounds__(T / 32 * 64, 1) void radial_bwd_dkdv_kernel(
         const int r = 2 * e + t, i = r / 4, jj = r % 4;
         float sv = sd_old.sd[0][r];
         // token-exact: okm holds the stage-2 block's allowed rows (bit r)
-        if constexpr (EXACT) sv = ((okm >> r) & 1u) ? sv : -INFINITY;
+        if constexpr (EXACT) sv = mask_bit(sv, okm, r);
         const float p = fast_exp2(fmaf(sv, scale_log2, rt[i][jj]));
         pd_new[0][r >> 3][r & 7] = bf16(p);
         pd_new[1][r >> 3][r & 7] = bf16(p * sd_old.sd[1][r]);
@@ -705,8 +716,7 @@ __global__ __launch_bounds__(T / 32 * 64 * (PAIR ? 2 : 1),
         // register r holds key kb*32 + 8*(r/4) + 4g + r%4 of the chunk
         if (masked) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (!((ok >> (16 * kb + r)) & 1u)) s[r] = -INFINITY;
+          for (int r = 0; r < 16; ++r) s[r] = mask_bit(s[r], ok, 16 * kb + r);
         }
         bf16x8 dsb[2];
 #pragma unroll
