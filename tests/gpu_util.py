@@ -129,6 +129,19 @@ def rounding_sigmas(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray,
                 dv=sg * np.sqrt((p ** 2).T @ do ** 2))
 
 
+def nan_outputs(B: int, H: int, N: int, D: int, grads: bool = True):
+    """Output buffers (O, LSE and, with grads, dQ, dK, dV) on the GPU filled
+    with NaN.  The kernels only store into them, so after a call every
+    element is finite exactly where some work item wrote it: a finiteness
+    check then shows that the launch covered every row."""
+    def nan(shape, dtype):
+        return torch.full(shape, float("nan"), dtype=dtype, device="cuda")
+    outs = [nan((B, H, N, D), torch.bfloat16), nan((B, H, N), torch.float32)]
+    if grads:
+        outs += [nan((B, H, N, D), torch.bfloat16) for _ in range(3)]
+    return outs
+
+
 def check_lse(got: np.ndarray, ref: np.ndarray, what: str = "lse"):
     assert np.isfinite(got).all(), f"{what}: non-finite values"
     err = float(np.abs(got - ref).max())

@@ -17,7 +17,7 @@ import torch
 
 import static_block_sparse_amd as sba
 import workloads
-from gpu_util import PEAKY_REL_MAX, check_close, check_lse, f64, sample_tiles
+from gpu_util import PEAKY_REL_MAX, check_close, check_lse, f64, nan_outputs, sample_tiles
 from oracle import attention as oa
 from oracle import mask as om
 
@@ -131,13 +131,14 @@ def test_backward_deterministic():
 def full_training_step():
     """The full-size training workload (66 frames x 3600 tokens, 24 heads,
     D = 128) run forward and backward in bench's launch configuration (every
-    batch and head in one launch)."""
+    batch and head in one launch), into outputs that start as NaN."""
     w = workloads.WORKLOADS["train_f66"]
     _say(f"[bwd-full] {w.name} B={w.B} H={w.H} N={w.N} D={w.D}")
     q, k, v, do = workloads.workload_inputs(w, device="cuda")
     L = sba.Layout(w.frames, w.tokens_per_frame, w.T)
-    o, lse = sba.attn_fwd(q, k, v, L, w.scale)
-    dq, dk, dv = sba.attn_bwd(q, k, v, o, lse, do, L, w.scale)
+    o, lse, dq, dk, dv = nan_outputs(w.B, w.H, w.N, w.D)
+    sba.attn_fwd(q, k, v, L, w.scale, out=o, lse=lse)
+    sba.attn_bwd(q, k, v, o, lse, do, L, w.scale, out=(dq, dk, dv))
     torch.cuda.synchronize()
     return dict(w=w, q=q, k=k, v=v, do=do, dq=dq, dk=dk, dv=dv)
 
@@ -145,6 +146,7 @@ def full_training_step():
 def test_full_size_training_step(full_training_step):
     r = full_training_step
     w, q, k, v, do, dq, dk, dv = (r[x] for x in ("w", "q", "k", "v", "do", "dq", "dk", "dv"))
+    # every gradient row was written
     for t in (dq, dk, dv):
         assert bool(torch.isfinite(t.float()).all())
     # identities over every head

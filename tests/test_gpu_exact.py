@@ -17,7 +17,7 @@ import torch
 
 import static_block_sparse_amd as sba
 import workloads
-from gpu_util import check_close, check_lse, f64, sample_tiles
+from gpu_util import check_close, check_lse, f64, nan_outputs, sample_tiles
 from oracle import attention as oa
 from oracle import mask as om
 
@@ -114,9 +114,11 @@ def test_exact_full_size_sampled_rows(name):
     _say(f"[exact-full] B={w.B} H={w.H} N={w.N} D={w.D}")
     q, k, v, do = workloads.workload_inputs(w, with_dout=True, device="cuda")
     L = sba.Layout(w.frames, w.tokens_per_frame, w.T, token_exact=True)
-    o, lse = sba.attn_fwd(q, k, v, L, w.scale)
-    dq, dk, dv = sba.attn_bwd(q, k, v, o, lse, do, L, w.scale)
+    o, lse, dq, dk, dv = nan_outputs(w.B, w.H, w.N, w.D)
+    sba.attn_fwd(q, k, v, L, w.scale, out=o, lse=lse)
+    sba.attn_bwd(q, k, v, o, lse, do, L, w.scale, out=(dq, dk, dv))
     torch.cuda.synchronize()
+    # the outputs started as NaN: every row was written
     for t in (o, lse, dq, dk, dv):
         assert bool(torch.isfinite(t.float()).all())
     tiles = sample_tiles(w.N, w.T, w.tokens_per_frame, seed=w.seed)

@@ -14,7 +14,7 @@ import torch
 
 import static_block_sparse_amd as sba
 import workloads
-from gpu_util import check_close, check_lse, f64, sample_tiles
+from gpu_util import check_close, check_lse, f64, nan_outputs, sample_tiles
 from oracle import attention as oa
 from oracle import mask as om
 
@@ -211,12 +211,13 @@ FULL = ["hunyuan_5s_720p", "wan21_720p", "hunyuan_4x_long", "train_f66"]
 def test_full_size_sampled_tiles(name):
     """Full-size workload, all heads in one launch (as bench.py times it);
     oracle check on sampled query tiles of the first and last heads; every
-    output finite."""
+    output row written (the outputs start as NaN)."""
     w = workloads.WORKLOADS[name]
     _say(f"[fwd-full] {name} B={w.B} H={w.H} N={w.N} D={w.D}")
     q, k, v = workloads.workload_inputs(w, with_dout=False, device="cuda")
     L = sba.Layout(w.frames, w.tokens_per_frame, w.T)
-    o, lse = sba.attn_fwd(q, k, v, L, w.scale)
+    o, lse = nan_outputs(w.B, w.H, w.N, w.D, grads=False)
+    sba.attn_fwd(q, k, v, L, w.scale, out=o, lse=lse)
     torch.cuda.synchronize()
     assert bool(torch.isfinite(lse).all())
     assert bool(torch.isfinite(o.float()).all())

@@ -17,7 +17,7 @@ import torch
 
 import static_block_sparse_amd as sba
 import workloads
-from gpu_util import check_close, check_lse, f64
+from gpu_util import check_close, check_lse, f64, nan_outputs
 from oracle import attention as oa
 from oracle import mask as om
 
@@ -89,8 +89,9 @@ def test_many_batch_heads(exact):
     q, k, v, do = workloads.make_inputs(B, H, N, D, 911, with_dout=True)
     L = sba.Layout(f, s, T, token_exact=exact)
     qc, kc, vc, dc = q.cuda(), k.cuda(), v.cuda(), do.cuda()
-    o, lse = sba.attn_fwd(qc, kc, vc, L, scale)
-    dq, dk, dv = sba.attn_bwd(qc, kc, vc, o, lse, dc, L, scale)
+    o, lse, dq, dk, dv = nan_outputs(B, H, N, D)
+    sba.attn_fwd(qc, kc, vc, L, scale, out=o, lse=lse)
+    sba.attn_bwd(qc, kc, vc, o, lse, dc, L, scale, out=(dq, dk, dv))
     torch.cuda.synchronize()
     kept = om.kept_tiles(f, s, T, True)
     mask = om.token_mask(f, s, True)
@@ -107,7 +108,9 @@ def test_many_batch_heads(exact):
         check_close(f64(dq[b, h]), rq, f"dQ b={b} h={h}", normalise=True)
         check_close(f64(dk[b, h]), rk, f"dK b={b} h={h}", normalise=True)
         check_close(f64(dv[b, h]), rv, f"dV b={b} h={h}", normalise=True)
+    # every row of every slice was written (the outputs started as NaN), and
     # each slice is its own: every output slice differs from its neighbours'
+    assert bool(torch.isfinite(lse).all())
     for t in (o, dq, dk, dv):
         assert bool(torch.isfinite(t.float()).all())
         assert not torch.equal(t[0, 0], t[0, 1]) and not torch.equal(t[1, 0], t[2, 0])
