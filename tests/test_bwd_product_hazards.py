@@ -136,8 +136,8 @@ def test_inline_assembly_products_are_far_from_their_readers(dkdv_assembly):
         assert min(reached) >= MIN_PRODUCTS_BETWEEN, (name, sorted(reached)[:8])
 
 
-def test_checker_flags_a_close_reader():
-    # the checker itself, on a hand-written sequence: a vector read of the
+def test_hazard_scan_flags_a_close_reader():
+    # the hazard scan itself, on a hand-written sequence: a vector read of the
     # result right after the product, or one product later, is caught; four
     # products later is not
     body_close = """
