@@ -127,14 +127,15 @@ def test_backward_deterministic():
         assert torch.equal(x, y)
 
 
-@pytest.fixture(scope="module")
-def full_training_step():
-    """The full-size training workload (66 frames x 3600 tokens, 24 heads,
-    D = 128) run forward and backward in bench's launch configuration (every
-    batch and head in one launch), into outputs that start as NaN."""
-    w = workloads.WORKLOADS["train_f66"]
+@pytest.fixture(scope="module", params=["train_f66", "hunyuan_5s_720p", "wan21_720p"])
+def full_backward(request):
+    """A full-size workload (the training step: 66 frames x 3600 tokens, 24
+    heads; HunyuanVideo 5 s 720p; Wan2.1 720p, 40 heads; D = 128) run forward
+    and backward in bench's launch configuration (every batch and head in one
+    launch), into outputs that start as NaN."""
+    w = workloads.WORKLOADS[request.param]
     _say(f"[bwd-full] {w.name} B={w.B} H={w.H} N={w.N} D={w.D}")
-    q, k, v, do = workloads.workload_inputs(w, device="cuda")
+    q, k, v, do = workloads.workload_inputs(w, with_dout=True, device="cuda")
     L = sba.Layout(w.frames, w.tokens_per_frame, w.T)
     o, lse, dq, dk, dv = nan_outputs(w.B, w.H, w.N, w.D)
     sba.attn_fwd(q, k, v, L, w.scale, out=o, lse=lse)
@@ -143,8 +144,8 @@ def full_training_step():
     return dict(w=w, q=q, k=k, v=v, do=do, dq=dq, dk=dk, dv=dv)
 
 
-def test_full_size_training_step(full_training_step):
-    r = full_training_step
+def test_full_size_backward(full_backward):
+    r = full_backward
     w, q, k, v, do, dq, dk, dv = (r[x] for x in ("w", "q", "k", "v", "do", "dq", "dk", "dv"))
     # every gradient row was written
     for t in (dq, dk, dv):
@@ -164,26 +165,27 @@ def test_full_size_training_step(full_training_step):
     kept = om.kept_tiles(w.frames, w.tokens_per_frame, w.T, True)
     for h in (0, w.H - 1):
         qh, kh, vh, dh = f64(q[0, h]), f64(k[0, h]), f64(v[0, h]), f64(do[0, h])
-        for u in sample_tiles(w.N, w.T, w.tokens_per_frame, seed=5)[:4]:
+        for u in sample_tiles(w.N, w.T, w.tokens_per_frame, seed=w.seed)[:4]:
             rows = slice(u * w.T, min(w.N, (u + 1) * w.T))
             rq = oa.bwd_dq_tile(qh, kh, vh, dh, kept, w.T, w.scale, u)
             check_close(f64(dq[0, h, rows]), rq, f"dQ h={h} tile={u}", normalise=True)
 
 
 @pytest.mark.timeout(900)
-def test_full_size_dkdv_tiles(full_training_step):
-    """dK and dV element by element at the full training workload, on key
-    tiles whose CSC columns take every path of the dK/dV walk: tile 0 (the
-    sink: every query tile of the sequence attends it, 1857 of them), tile
-    28 (straddles frames 0 and 1), the last, partial key tile (16 valid
-    keys) and one random tile of the first head, and the last tile of the
-    last head.  The oracle takes each row's full softmax over its own kept
-    keys, so the sink columns need the row terms of the whole head."""
+def test_full_size_dkdv_tiles(full_backward):
+    """dK and dV element by element at a full-size workload, on key tiles
+    whose CSC columns take every path of the dK/dV walk: tile 0 (the sink:
+    every query tile of the sequence attends it, 1857 of them in the
+    training step), tile 28 (straddles frames 0 and 1), the last, partial
+    key tile (32, 16 and 80 valid keys in the three workloads) and one
+    random tile of the first head, and the last tile of the last head.  The
+    oracle takes each row's full softmax over its own kept keys, so the sink
+    columns need the row terms of the whole head."""
     from concurrent.futures import ThreadPoolExecutor
 
     from threadpoolctl import threadpool_limits
 
-    r = full_training_step
+    r = full_backward
     w, q, k, v, do, dk, dv = (r[x] for x in ("w", "q", "k", "v", "do", "dk", "dv"))
     kept = om.kept_tiles(w.frames, w.tokens_per_frame, w.T, True)
     nb = kept.shape[0]
