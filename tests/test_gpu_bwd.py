@@ -127,10 +127,12 @@ def test_backward_deterministic():
         assert torch.equal(x, y)
 
 
-@pytest.fixture(scope="module", params=["train_f66", "hunyuan_5s_720p", "wan21_720p"])
+@pytest.fixture(scope="module",
+                params=["train_f66", "hunyuan_5s_720p", "wan21_720p", "hunyuan_4x_long"])
 def full_backward(request):
     """A full-size workload (the training step: 66 frames x 3600 tokens, 24
-    heads; HunyuanVideo 5 s 720p; Wan2.1 720p, 40 heads; D = 128) run forward
+    heads; HunyuanVideo 5 s 720p; Wan2.1 720p, 40 heads; 129 frames, the
+    longest; D = 128) run forward
     and backward in bench's launch configuration (every batch and head in one
     launch), into outputs that start as NaN."""
     w = workloads.WORKLOADS[request.param]
@@ -176,8 +178,8 @@ def test_full_size_dkdv_tiles(full_backward):
     """dK and dV element by element at a full-size workload, on key tiles
     whose CSC columns take every path of the dK/dV walk: tile 0 (the sink:
     every query tile of the sequence attends it, 1857 of them in the
-    training step), tile 28 (straddles frames 0 and 1), the last, partial
-    key tile (32, 16 and 80 valid keys in the three workloads) and one
+    training step, 3629 at 129 frames), tile 28 (straddles frames 0 and 1),
+    the last, partial key tile (32, 16, 80 and 16 valid keys) and one
     random tile of the first head, and the last tile of the last head.  The
     oracle takes each row's full softmax over its own kept keys, so the sink
     columns need the row terms of the whole head."""
