@@ -34,8 +34,9 @@ frame sizes where ceil and floor of 2^r / s differ, by its structure (empty
 or diagonal blocks) and the band density bound (2^-r / 2, 2^-r]; the pages
 give no worked numbers for it, so the exact period inside that bound is
 parity unpinned.  ``attention.bwd_dkdv_tile`` / ``row_stats`` (per key tile)
-and ``fwd_rows`` / ``dq_rows`` (per query row set) are pinned against the
-whole-head functions and torch float64 autograd.
+and ``fwd_rows`` / ``dq_rows`` (per query row set), and their token-mask
+counterparts ``dkdv_masked_keys`` / ``row_stats_masked``, are pinned against
+the whole-head functions and torch float64 autograd.
 """
 
 from . import mask, attention  # noqa: F401

@@ -199,3 +199,39 @@ def bwd_dkdv_tile(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray,
         dv += p.T @ do[rows]
         dk += scale * (ds.T @ q[rows])
     return dk, dv
+
+
+def row_stats_masked(q_rows: np.ndarray, k_cols: np.ndarray, v_cols: np.ndarray,
+                     do_rows: np.ndarray, mask_rows: np.ndarray,
+                     scale: float) -> tuple[np.ndarray, np.ndarray]:
+    """LSE and Delta of some query rows under their rows of a boolean token
+    mask, restricted to key columns that hold every key the rows may attend
+    (k_cols, v_cols [c, D]; mask_rows [r, c]): the row terms of the textbook
+    gradient, as ``row_stats`` gives them under the tile map."""
+    o, lse = fwd_masked(q_rows, k_cols, v_cols, mask_rows, scale)
+    return lse, (do_rows * o).sum(axis=1)
+
+
+def dkdv_masked_keys(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray,
+                     keys: slice, blocks, scale: float) -> tuple[np.ndarray, np.ndarray]:
+    """dK and dV [keys, D] of the key rows ``keys`` under a boolean token mask.
+
+    ``blocks``: tuples (rows, allowed, lse, delta) over groups of query rows
+    that together hold every query row the mask lets attend one of these
+    keys; ``allowed`` [len(rows), len(keys)] is the mask restricted to those
+    rows and keys, and lse, delta are the rows' terms over all of their
+    allowed keys (``row_stats_masked``).  The textbook formulas restricted
+    to the keys: P = exp(scale <Q, K> - LSE) where allowed (0 elsewhere),
+    dV = P^T dO and dK = scale (P (dP - Delta))^T Q with dP = dO V^T.
+    """
+    nk, d = keys.stop - keys.start, q.shape[1]
+    dk = np.zeros((nk, d))
+    dv = np.zeros((nk, d))
+    for rows, allowed, lse, delta in blocks:
+        z = scale * (q[rows] @ k[keys].T)
+        p = np.where(allowed, np.exp(np.where(allowed, z, 0.0) - lse[:, None]), 0.0)
+        dp = do[rows] @ v[keys].T
+        ds = p * (dp - delta[:, None])
+        dv += p.T @ do[rows]
+        dk += scale * (ds.T @ q[rows])
+    return dk, dv

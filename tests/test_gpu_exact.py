@@ -6,7 +6,8 @@ must equal plain attention under the token mask (oracle ``fwd_masked`` /
 ``bwd_masked`` with ``token_mask``).  Small shapes are compared element by
 element over every head; the full-size 720p workload and the 129-frame one
 (where more than half of the kept tiles are partial) on sampled query rows
-(forward O/LSE and dQ) and through the gradient identities.
+(forward O/LSE and dQ) and through the gradient identities, and at 720p dK
+and dV element by element on sampled key tiles.
 """
 
 import sys
@@ -142,3 +143,61 @@ def test_exact_full_size_sampled_rows(name):
     assert float((sdv - sdo).abs().max()) <= tol, (float((sdv - sdo).abs().max()), tol)
     rms_dk = float(dk.double().pow(2).mean().sqrt())
     assert float(dk.double().sum(dim=2).abs().max()) <= 4 * np.sqrt(w.N) * 2.0 ** -8 * rms_dk + 1e-6
+
+
+@pytest.mark.timeout(900)
+def test_exact_full_size_dkdv_tiles():
+    """720p (33 frames x 3600 tokens, 24 heads in one launch) in token-exact
+    mode: dK and dV element by element against the token oracle on key
+    tiles 0 (the sink: every query row attends all of its keys), 28
+    (straddles frames 0 and 1), the last, partial tile (16 keys) and one
+    random tile of the first head, and the last tile of the last head.  Each
+    attending row's LSE and Delta come from its own allowed keys (within its
+    kept tiles, which hold all of them)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    from threadpoolctl import threadpool_limits
+
+    w = workloads.WORKLOADS["hunyuan_5s_720p"]
+    f, s, T, n = w.frames, w.tokens_per_frame, w.T, w.N
+    _say(f"[exact-dkdv] B={w.B} H={w.H} N={n} D={w.D}")
+    q, k, v, do = workloads.workload_inputs(w, with_dout=True, device="cuda")
+    L = sba.Layout(f, s, T, token_exact=True)
+    o, lse, dq, dk, dv = nan_outputs(w.B, w.H, n, w.D)
+    sba.attn_fwd(q, k, v, L, w.scale, out=o, lse=lse)
+    sba.attn_bwd(q, k, v, o, lse, do, L, w.scale, out=(dq, dk, dv))
+    torch.cuda.synchronize()
+    kept = om.kept_tiles(f, s, T, True)
+    nb = kept.shape[0]
+    frame0_tiles = -(-s // T)
+    rand = int(np.random.default_rng(11).integers(frame0_tiles, nb - 1))
+    cases = {0: [0, frame0_tiles - 1, nb - 1, rand], w.H - 1: [nb - 1]}
+    key_range = {vt: slice(vt * T, min(n, (vt + 1) * T)) for vt in range(nb)}
+    workers = 16
+    for h, tiles in cases.items():
+        qh, kh, vh, dh = f64(q[0, h]), f64(k[0, h]), f64(v[0, h]), f64(do[0, h])
+        need = sorted(set(int(u) for vt in tiles for u in np.nonzero(kept[:, vt])[0]))
+        _say(f"[exact-dkdv] head {h}: key tiles {tiles}, row terms of {len(need)} query tiles")
+
+        def block_of(u):
+            rows = np.arange(u * T, min(n, (u + 1) * T))
+            cols = oa.tile_columns(kept[u], n, T)
+            m = om.token_mask_rows(f, s, rows)
+            lse_u, delta_u = oa.row_stats_masked(qh[rows], kh[cols], vh[cols], dh[rows],
+                                                 m[:, cols], w.scale)
+            return u, rows, lse_u, delta_u, {vt: m[:, key_range[vt]] for vt in tiles
+                                             if kept[u, vt]}
+
+        blocks = {vt: [] for vt in tiles}
+        with threadpool_limits(1), ThreadPoolExecutor(workers) as ex:
+            for u, rows, lse_u, delta_u, allowed in ex.map(block_of, need):
+                for vt, a in allowed.items():
+                    blocks[vt].append((rows, a, lse_u, delta_u))
+        for vt in tiles:
+            keys = key_range[vt]
+            rk, rv = oa.dkdv_masked_keys(qh, kh, vh, dh, keys, blocks[vt], w.scale)
+            sk = check_close(f64(dk[0, h, keys]), rk, f"dK h={h} key tile={vt}", normalise=True)
+            sv = check_close(f64(dv[0, h, keys]), rv, f"dV h={h} key tile={vt}", normalise=True)
+            _say(f"[exact-dkdv] head {h} key tile {vt} ({len(blocks[vt])} query tiles): "
+                 f"dK max {sk['max_abs']:.3g} (rms {sk['rms_ref']:.3g}), "
+                 f"dV max {sv['max_abs']:.3g} (rms {sv['rms_ref']:.3g})")

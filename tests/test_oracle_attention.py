@@ -205,3 +205,57 @@ def test_row_stats_are_the_row_terms():
         np.testing.assert_allclose(lse, lse_all[rows], rtol=0, atol=1e-13)
         np.testing.assert_allclose(delta, (p * (do[rows] @ v[cols].T)).sum(axis=1),
                                    rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("f,s,T,sink", [(6, 11, 8, True), (5, 30, 16, False), (9, 7, 4, True),
+                                        (4, 5, 16, True), (3, 40, 64, False)])
+def test_dkdv_masked_keys_matches_autograd(f, s, T, sink):
+    # per key tile under the token mask, with each row's terms taken over the
+    # keys of its kept tiles only (as at full size), against torch float64
+    # autograd of the masked softmax over the whole head and the whole-head
+    # oracle backward
+    n, d = f * s, 6
+    q, k, v, do = (_rand((n, d), 90 + i) for i in range(4))
+    mask = om.token_mask(f, s, sink)
+    kept = om.kept_tiles(f, s, T, sink)
+    nb = kept.shape[0]
+    scale = 0.7
+    tq, tk, tv = (torch.from_numpy(x.copy()).requires_grad_() for x in (q, k, v))
+    z = (scale * tq @ tk.T).masked_fill(~torch.from_numpy(mask), float("-inf"))
+    (torch.softmax(z, dim=1) @ tv).backward(torch.from_numpy(do))
+    _, dk_all, dv_all = oa.bwd_masked(q, k, v, do, mask, scale)
+    blocks_of = {}
+    for u in range(nb):
+        rows = slice(u * T, min(n, (u + 1) * T))
+        cols = oa.tile_columns(kept[u], n, T)
+        lse, delta = oa.row_stats_masked(q[rows], k[cols], v[cols], do[rows],
+                                         mask[rows][:, cols], scale)
+        blocks_of[u] = (rows, lse, delta)
+    for vt in range(nb):
+        keys = slice(vt * T, min(n, (vt + 1) * T))
+        blocks = [(r, mask[r, keys], lse, delta)
+                  for u, (r, lse, delta) in blocks_of.items() if kept[u, vt]]
+        gk, gv = oa.dkdv_masked_keys(q, k, v, do, keys, blocks, scale)
+        np.testing.assert_allclose(gk, tk.grad.numpy()[keys], rtol=0, atol=1e-11)
+        np.testing.assert_allclose(gv, tv.grad.numpy()[keys], rtol=0, atol=1e-11)
+        np.testing.assert_allclose(gk, dk_all[keys], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(gv, dv_all[keys], rtol=0, atol=1e-12)
+
+
+def test_dkdv_masked_keys_needs_every_attending_row():
+    # leaving out one query tile that attends a key tile changes its
+    # gradient: the function sums over exactly the blocks it is given
+    f, s, T, d = 5, 13, 8, 4
+    n = f * s
+    q, k, v, do = (_rand((n, d), 95 + i) for i in range(4))
+    mask = om.token_mask(f, s, True)
+    scale = 0.8
+    keys = slice(0, T)
+    blocks = []
+    for u in range(-(-n // T)):
+        rows = slice(u * T, min(n, (u + 1) * T))
+        lse, delta = oa.row_stats_masked(q[rows], k, v, do[rows], mask[rows], scale)
+        blocks.append((rows, mask[rows, keys], lse, delta))
+    full_k, full_v = oa.dkdv_masked_keys(q, k, v, do, keys, blocks, scale)
+    part_k, part_v = oa.dkdv_masked_keys(q, k, v, do, keys, blocks[:-1], scale)
+    assert np.abs(full_v - part_v).max() > 1e-3 and np.abs(full_k - part_k).max() > 1e-3
