@@ -43,7 +43,10 @@ extern "C" {
 enum {
   RADIAL_OK = 0,
   RADIAL_E_INVALID = -1,     /* null / misaligned pointer, bad scalar value   */
-  RADIAL_E_UNSUPPORTED = -2, /* (D, block_size) pair without a compiled kernel */
+  RADIAL_E_UNSUPPORTED = -2, /* (D, block_size) without a kernel, or a size  */
+                             /* beyond a stated limit (a slice of 2^31 bytes */
+                             /* or more, rows beyond the allocation-free     */
+                             /* backward's scratch)                          */
   RADIAL_E_SHAPE = -3,       /* N differs from frames * tokens_per_frame       */
   RADIAL_E_NOMEM = -4,       /* host or device allocation failed               */
   RADIAL_E_HIP = -5,         /* a HIP runtime call or kernel launch failed     */

@@ -449,7 +449,7 @@ const char *radial_status_string(int status) {
   switch (status) {
     case RADIAL_OK: return "ok";
     case RADIAL_E_INVALID: return "invalid argument";
-    case RADIAL_E_UNSUPPORTED: return "unsupported (D, block_size)";
+    case RADIAL_E_UNSUPPORTED: return "unsupported shape or size";
     case RADIAL_E_SHAPE: return "shape mismatch";
     case RADIAL_E_NOMEM: return "out of memory";
     case RADIAL_E_HIP: return "HIP error";

@@ -252,6 +252,7 @@ def test_compute_calls_validate_before_touching_the_gpu():
     b = (L.handle, 1, 1, 2000, 64, 0.125) + (dummy,) * 10 + (ws, None)
     assert lib.radial_attn_bwd(*b) == -3
     assert lib.radial_status_string(-3) == b"shape mismatch"
+    assert lib.radial_status_string(-2) == b"unsupported shape or size"
     # the allocation-free backward validates the same way
     nb_ = (L.handle, 1, 1, 2048, 64, 0.125) + (dummy,) * 9 + (None,)
     assert lib.radial_attn_bwd_noalloc(*nb_) == -6
