@@ -25,7 +25,8 @@ head, divided by the measured step time.  Extra objects:
                   on the same workload;
   train        -- the training step (66 frames x 3600 tokens, H=24): forward,
                   backward (dQ, dK, dV from a random dO) and their total,
-                  10 * D flops per kept pair for the backward;
+                  10 * D flops per kept pair for the backward (bwd_hw_frac:
+                  the 14 * D per pair of matrix work its kernels issue);
   others       -- the HunyuanVideo 5 s 720p and Wan2.1 720p forwards (and
                   the 720p backward);
   token_exact  -- 720p forward and backward with token-exact masking inside
@@ -347,7 +348,10 @@ def main():
             "bwd_frac": round(bf / bms / 1e9 / PEAK_BF16_TFLOPS, 4),
             "total_frac": round((ff + bf) / (fms + bms) / 1e9 / PEAK_BF16_TFLOPS, 4),
             "fwd_alg_flops": ff, "bwd_alg_flops": bf,
-            "bwd_flop_convention": "10 * D per kept token pair (4 * D forward)"}
+            "bwd_flop_convention": "10 * D per kept token pair (4 * D forward)",
+            # the matrix work the backward kernels issue: S and dP are computed
+            # in both the dK/dV and the dQ kernel (8 D + 6 D per kept pair)
+            "bwd_hw_frac": round(14 * tw.D * tpairs / bms / 1e9 / PEAK_BF16_TFLOPS, 4)}
         del q, k, v, o, lse, do, ws
         torch.cuda.empty_cache()
 
