@@ -230,3 +230,29 @@ def test_full_size_sampled_tiles(name):
             ro, rl = oa.fwd_tile(qh, kh, vh, kept, w.T, w.scale, u)
             check_close(f64(o[0, h, rows]), ro, f"{name} O h={h} tile={u}")
             check_lse(f64(lse[0, h, rows]), rl, f"{name} lse h={h} tile={u}")
+
+
+def test_dense_layout_full_size_sampled_tiles():
+    """The in-repo dense kernel (the same kernel on a layout that keeps every
+    tile) at the 4x HunyuanVideo size bench.py compares against, all heads
+    in one launch: sampled query tiles of the first and last heads against
+    the oracle over all keys; every output row written."""
+    w = workloads.WORKLOADS["hunyuan_4x_long"]
+    _say(f"[fwd-dense-full] {w.name} B={w.B} H={w.H} N={w.N} D={w.D}")
+    q, k, v = workloads.workload_inputs(w, with_dout=False, device="cuda")
+    L = sba.Layout(w.frames, w.tokens_per_frame, w.T, dense=True)
+    assert L.nnz_tiles == L.n_blocks ** 2
+    o, lse = nan_outputs(w.B, w.H, w.N, w.D, grads=False)
+    sba.attn_fwd(q, k, v, L, w.scale, out=o, lse=lse)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(lse).all())
+    assert bool(torch.isfinite(o.float()).all())
+    kept = np.ones((L.n_blocks,) * 2, bool)
+    tiles = sample_tiles(w.N, w.T, w.tokens_per_frame, seed=w.seed + 100)
+    for h in (0, w.H - 1):
+        qh, kh, vh = f64(q[0, h]), f64(k[0, h]), f64(v[0, h])
+        for u in tiles:
+            rows = slice(u * w.T, min(w.N, (u + 1) * w.T))
+            ro, rl = oa.fwd_tile(qh, kh, vh, kept, w.T, w.scale, u)
+            check_close(f64(o[0, h, rows]), ro, f"dense O h={h} tile={u}")
+            check_lse(f64(lse[0, h, rows]), rl, f"dense lse h={h} tile={u}")
